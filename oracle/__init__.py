@@ -1,0 +1,9 @@
+"""Float64 CPU oracle of the DSA decode step -- test infrastructure only.
+
+Imported by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py``; never by the library.
+"""
+from .dsa_oracle import (  # noqa: F401
+    e4m3fn_decode, bf16_decode, row_extents, token_location, indexer_keys,
+    indexer_logits, topk_row, topk, sparse_mla, sparse_mla_split, MASK_SENTINEL,
+)

@@ -1,0 +1,283 @@
+"""Reference oracle for the DeepSeek-Sparse-Attention decode step (TEST INFRASTRUCTURE).
+
+This is a plain, slow, CPU implementation in float64, used only by the test
+suite, the package smoke check and the CPU-baseline leg of the benchmark to
+decide whether the HIP library is right.  The library never imports it and
+has no fallback to it.  It shares no code with the GPU path.
+
+What it computes, and where each step comes from:
+
+* FP8 decode.  The vLLM PR page "[Feature] TRITON_MLA_SPARSE backend for
+  SM8x/11x/12x DSA Sparse MLA Support" (section Changes, item 2; section Tests)
+  keeps the indexer K cache and q in FP8 and tests the decode of all 256 byte
+  values.  The format is OCP E4M3 "fn" (bias 7, no infinities, one NaN pattern
+  per sign): written out in ``e4m3fn_decode``.
+* Indexer ("lightning indexer") logits.  Same page, Changes item 2: MQA logits
+  from fp8 q and paged fp8 K, with the per-token K scale applied to the fp32
+  dot output, 64 indexer heads of dim 128 reduced with per-head weights.  The
+  pages name but do not print the head reduction; the reading taken is
+  logit[r, s] = sum_h w[r, h] * relu(q[r, h] . k[s]) * kscale[s]
+  (the DSA lightning-indexer form; without a per-head nonlinearity the 64 heads
+  would collapse into one dot).  A token whose block maps to a page outside
+  the cache is never read and its logit is -inf.  Row r of a sequence with L
+  cached tokens and q_len queries sees keys [0, L - q_len + i + 1) ("per-row causal" bound).
+  Keys come through the block table, 64 tokens per block (vllm-dsa-mtp-sm80
+  README: pages addressed through their stride).
+* Top-k.  The PR page review thread (chunked exact top-k discussion): the
+  index_topk = 2048 largest logits of each row.  Order: larger value first,
+  equal values to the lower index; the chosen indices are written in ascending
+  index order, padded with -1 when a row has fewer than k keys.
+* Sparse MLA.  Same page, Changes item 3: attention of each query row over only
+  its selected latent rows, split-KV partials merged N-way by online softmax, a
+  single-pass fast path, and -1e30 as the running-max sentinel of fully masked
+  tiles.  Score z = scale * q[h, :576] . c[s, :576]; value = c[s, :512];
+  out = softmax(z) @ V; lse = ln sum exp(z) (natural log).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64
+IDX_HEADS = 64
+IDX_DIM = 128
+IDX_SCALE_OFFSET = PAGE * IDX_DIM
+KV_DIM = 576
+V_DIM = 512
+MASK_SENTINEL = -1e30
+
+
+# --------------------------------------------------------------------------
+# element decoding
+
+def e4m3fn_decode(codes) -> np.ndarray:
+    """OCP E4M3 ("e4m3fn") byte -> float64.
+
+    sign s = bit 7, exponent e = bits 6..3 (bias 7), mantissa m = bits 2..0.
+    e == 0: subnormal (-1)^s * m * 2^-9.  e == 15 and m == 7: NaN (no
+    infinities).  Otherwise (-1)^s * (8 + m) * 2^(e - 10), i.e. 1.m * 2^(e-7).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = c >> 7
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(s == 1, -mag, mag)
+
+
+def bf16_decode(u16) -> np.ndarray:
+    """bfloat16 bit pattern -> float64 (the upper half of an IEEE binary32)."""
+    u = np.asarray(u16).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# batch geometry
+
+def row_extents(seq_lens, query_start):
+    """(sequence of each row, e_r) with e_r = L_b - q_len_b + i + 1, floored at 0."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    qs = np.asarray(query_start, dtype=np.int64)
+    R = int(qs[-1])
+    seq = np.zeros(R, dtype=np.int64)
+    ext = np.zeros(R, dtype=np.int64)
+    for b in range(len(seq_lens)):
+        q = int(qs[b + 1] - qs[b])
+        for i in range(q):
+            r = int(qs[b]) + i
+            seq[r] = b
+            ext[r] = max(0, int(seq_lens[b]) - q + i + 1)
+    return seq, ext
+
+
+def token_location(block_table_row, s):
+    """Physical page and slot of logical token s: block s // 64, slot s % 64."""
+    s = np.asarray(s, dtype=np.int64)
+    return np.asarray(block_table_row, dtype=np.int64)[s // PAGE], s % PAGE
+
+
+# --------------------------------------------------------------------------
+# indexer logits
+
+def indexer_keys(idx_cache, block_table_row, s):
+    """Codes [n, 128] and fp32 scales [n] (as float64) of the logical tokens in s.
+
+    An indexer page holds its 64 tokens' 128 e4m3 codes, then their 64 fp32
+    scales starting at byte 8192 of the page.
+    """
+    cache = np.asarray(idx_cache, dtype=np.uint8)
+    page, slot = token_location(block_table_row, s)
+    codes = cache[page[:, None], slot[:, None] * IDX_DIM + np.arange(IDX_DIM)[None, :]]
+    sc_cols = IDX_SCALE_OFFSET + 4 * slot[:, None] + np.arange(4)[None, :]
+    scale_bytes = np.ascontiguousarray(cache[page[:, None], sc_cols])
+    return codes, scale_bytes.view(np.float32).reshape(len(page)).astype(np.float64)
+
+
+def indexer_logits(q_fp8, weights, idx_cache, block_table, seq_lens, query_start,
+                   logits_stride, clean=True, rows=None):
+    """Logits and magnitudes of the lightning indexer.
+
+    Returns (logits, magnitude, e) where logits[r, s] for s < e_r is
+    sum_h w[r,h] * max(q_h . k_s, 0) * kscale_s, magnitude[r, s] is the same sum
+    with |w[r,h]| (the scale the comparison tolerance is relative to), and
+    columns s >= e_r hold -inf when ``clean`` and NaN (meaning: not written)
+    otherwise.  ``rows`` restricts the computation to a subset of rows (the
+    others stay NaN).
+    """
+    q_fp8 = np.asarray(q_fp8, dtype=np.uint8)
+    w = np.asarray(weights, dtype=np.float64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    seq, ext = row_extents(seq_lens, query_start)
+    R = len(ext)
+    logits = np.full((R, logits_stride), np.nan)
+    mag = np.full((R, logits_stride), np.nan)
+    num_pages = np.asarray(idx_cache).shape[0]
+    for r in (range(R) if rows is None else rows):
+        e = int(ext[r])
+        if clean:
+            logits[r, e:] = -np.inf
+        if e == 0:
+            continue
+        page, _ = token_location(bt[seq[r]], np.arange(e))
+        ok = (page >= 0) & (page < num_pages)
+        logits[r, :e] = -np.inf                # tokens on an out-of-range page stay masked
+        mag[r, :e] = 0.0
+        if not ok.any():
+            continue
+        s = np.nonzero(ok)[0]
+        codes, scales = indexer_keys(idx_cache, bt[seq[r]], s)
+        Q = e4m3fn_decode(q_fp8[r])            # [64, 128]
+        K = e4m3fn_decode(codes)               # [n, 128]
+        relu = np.maximum(Q @ K.T, 0.0)        # [64, n]
+        logits[r, s] = (w[r] @ relu) * scales
+        mag[r, s] = (np.abs(w[r]) @ relu) * scales
+    return logits, mag, ext
+
+
+# --------------------------------------------------------------------------
+# top-k
+
+def topk_row(values, e, k):
+    """Indices of the k largest of values[0:e] (ties to the lower index), ascending, -1 padded."""
+    v = np.asarray(values[:e], dtype=np.float64)
+    n = min(int(k), int(e))
+    out = np.full(int(k), -1, dtype=np.int64)
+    if n == 0:
+        return out
+    order = np.lexsort((np.arange(e), -v))     # primary: -v ascending; secondary: index
+    out[:n] = np.sort(order[:n])
+    return out
+
+
+def topk(logits, seq_lens, query_start, k, rows=None):
+    """top-k of every row over its own causal extent."""
+    _, ext = row_extents(seq_lens, query_start)
+    R = len(ext)
+    out = np.full((R, int(k)), -1, dtype=np.int64)
+    for r in (range(R) if rows is None else rows):
+        out[r] = topk_row(logits[r], int(ext[r]), k)
+    return out
+
+
+# --------------------------------------------------------------------------
+# sparse MLA
+
+def _selected_rows(kv_cache, bt_row, idx_list, e, num_pages):
+    """Latent rows [n, 576] (float64) of the valid entries of an index list.
+
+    Valid entries are 0 <= s < e whose block maps to a page in [0, num_pages);
+    everything else (the -1 padding included) is masked and never read.
+    Duplicates are kept, in list order.
+    """
+    kv = np.asarray(kv_cache)
+    s = np.asarray(idx_list, dtype=np.int64)
+    s = s[(s >= 0) & (s < e)]
+    if s.size == 0:
+        return np.zeros((0, KV_DIM))
+    page, slot = token_location(bt_row, s)
+    ok = (page >= 0) & (page < num_pages)
+    page, slot = page[ok], slot[ok]
+    cols = slot[:, None] * KV_DIM + np.arange(KV_DIM)[None, :]
+    return bf16_decode(kv[page[:, None], cols])
+
+
+def sparse_mla(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
+               softmax_scale, num_pages=None, rows=None):
+    """Single-pass sparse MLA: (out [R, H, 512] float64, lse [R, H] float64).
+
+    For each row and head over the row's valid selected latent rows c_j:
+    z_j = scale * q . c_j (576 dims); out = sum softmax(z)_j c_j[:512];
+    lse = ln sum_j exp(z_j).  A row with no valid entry gives out = 0 and
+    lse = -inf.
+    """
+    q_u16 = np.asarray(q_mla)
+    R, H, _ = q_u16.shape
+    bt = np.asarray(block_table, dtype=np.int64)
+    if num_pages is None:
+        num_pages = int(np.asarray(kv_cache).shape[0])
+    seq, ext = row_extents(seq_lens, query_start)
+    out = np.zeros((R, H, V_DIM))
+    lse = np.full((R, H), -np.inf)
+    for r in (range(R) if rows is None else rows):
+        C = _selected_rows(kv_cache, bt[seq[r]], indices[r], int(ext[r]), num_pages)
+        if C.shape[0] == 0:
+            continue
+        Q = bf16_decode(q_u16[r])                       # [H, 576]
+        z = softmax_scale * (Q @ C.T)                   # [H, n]
+        M = z.max(axis=1, keepdims=True)
+        p = np.exp(z - M)
+        l = p.sum(axis=1, keepdims=True)
+        out[r] = (p @ C[:, :V_DIM]) / l
+        lse[r] = (M + np.log(l))[:, 0]
+    return out, lse
+
+
+def sparse_mla_split(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
+                     softmax_scale, num_splits, num_pages=None, rows=None):
+    """Split-KV sparse MLA with the N-way online-softmax merge.
+
+    The k slots of each row's index list are cut into ``num_splits`` contiguous
+    ranges of ceil(k / num_splits) slots.  Each range yields a running max m_i
+    (starting from the -1e30 sentinel, so an all-masked range never forms
+    (-inf) - (-inf)), a sum l_i = sum exp(z - m_i) and an unnormalised
+    accumulator acc_i = sum exp(z - m_i) c[:512].  The merge takes
+    M = max m_i, L = sum l_i exp(m_i - M), out = sum acc_i exp(m_i - M) / L and
+    lse = M + ln L; L == 0 (nothing valid anywhere) gives out = 0, lse = -inf.
+    """
+    q_u16 = np.asarray(q_mla)
+    R, H, _ = q_u16.shape
+    idx = np.asarray(indices, dtype=np.int64)
+    k = idx.shape[1]
+    bt = np.asarray(block_table, dtype=np.int64)
+    if num_pages is None:
+        num_pages = int(np.asarray(kv_cache).shape[0])
+    seq, ext = row_extents(seq_lens, query_start)
+    per = -(-k // num_splits)
+    out = np.zeros((R, H, V_DIM))
+    lse = np.full((R, H), -np.inf)
+    for r in (range(R) if rows is None else rows):
+        Q = bf16_decode(q_u16[r])
+        ms, ls, accs = [], [], []
+        for i in range(num_splits):
+            C = _selected_rows(kv_cache, bt[seq[r]], idx[r, i * per:(i + 1) * per],
+                               int(ext[r]), num_pages)
+            m = np.full(H, MASK_SENTINEL)
+            l = np.zeros(H)
+            acc = np.zeros((H, V_DIM))
+            if C.shape[0]:
+                z = softmax_scale * (Q @ C.T)
+                m = np.maximum(m, z.max(axis=1))
+                p = np.exp(z - m[:, None])
+                l = p.sum(axis=1)
+                acc = p @ C[:, :V_DIM]
+            ms.append(m)
+            ls.append(l)
+            accs.append(acc)
+        M = np.max(ms, axis=0)
+        wts = [np.exp(m - M) for m in ms]
+        L = sum(l * wt for l, wt in zip(ls, wts))
+        A = sum(a * wt[:, None] for a, wt in zip(accs, wts))
+        ok = L > 0
+        out[r][ok] = A[ok] / L[ok][:, None]
+        lse[r][ok] = M[ok] + np.log(L[ok])
+    return out, lse
