@@ -1,0 +1,212 @@
+"""Benchmark of one DSA decode step on one MI355X.
+
+A step is the whole hot path for one batch: lightning-indexer logits over the
+paged fp8 K cache, per-row top-2048, and sparse MLA over the selected latent
+rows (split-KV partials + merge when the split heuristic picks more than one).
+Inputs are seeded synthetic tensors resident in HBM before timing starts; the
+timed steps rotate through several copies of the caches so that the 256 MB
+Infinity Cache cannot serve one step's reads from the previous step.
+
+Prints one JSON line (metric, value = steps/s, roofline of the dominant kernel,
+the float64 oracle timed on the host as cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate through (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--splits", type=int, default=0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl):
+    """Bytes each stage must move at minimum (inputs read once, outputs written once)."""
+    seq_lens = wl.seq_lens.numpy().astype(np.int64)
+    qs = wl.query_start.numpy().astype(np.int64)
+    q_lens = qs[1:] - qs[:-1]
+    _, ext = _row_extents(seq_lens, qs)
+    k, H = wl.topk, wl.num_heads
+    idx_in = int((132 * seq_lens + q_lens * 64 * (128 + 4) + 4 * ((seq_lens + 63) // 64)).sum())
+    logit_bytes = int(4 * ext.sum())
+    sel = np.minimum(ext, k)
+    mla = int((1152 * sel + 4 * k + H * (1152 + 1024 + 4)).sum())
+    return {"indexer": idx_in + logit_bytes, "topk": logit_bytes + 4 * k * len(ext), "sparse_mla": mla,
+            "indexer_flops": int(16384 * ext.sum()),
+            "mla_flops": int(2 * H * (576 + 512) * sel.sum())}
+
+
+def _row_extents(seq_lens, qs):
+    R = int(qs[-1])
+    seq = np.zeros(R, np.int64)
+    ext = np.zeros(R, np.int64)
+    for b in range(len(seq_lens)):
+        q = int(qs[b + 1] - qs[b])
+        for i in range(q):
+            seq[qs[b] + i] = b
+            ext[qs[b] + i] = max(0, int(seq_lens[b]) - q + i + 1)
+    return seq, ext
+
+
+def cpu_baseline(wl, budget_s):
+    """Time the float64 oracle on a bounded, seeded sample of the step's rows."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    R = wl.num_rows
+    rng = np.random.default_rng(0)
+    order = rng.permutation(R)
+    q8, w, cache = wl.q_fp8.numpy(), wl.weights.numpy(), wl.idx_cache.numpy()
+    bt, sl, qs = wl.block_table.numpy(), wl.seq_lens.numpy(), wl.query_start.numpy()
+    qm, kv = wl.q_mla.view(torch.int16).numpy(), wl.kv_cache.view(torch.int16).numpy()
+    stride = wl.max_seq_len
+    done, t0 = 0, time.perf_counter()
+    for r in order:
+        lg, _, _ = oracle.indexer_logits(q8, w, cache, bt, sl, qs, stride, rows=[int(r)])
+        idx = oracle.topk(lg, sl, qs, wl.topk, rows=[int(r)])
+        oracle.sparse_mla(qm, kv, bt, sl, qs, idx, wl.softmax_scale, rows=[int(r)])
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    steps_per_s = (done / R) / dt
+    return {"value": steps_per_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {R} rows of one step (indexer+top-k+sparse MLA per row, float64 numpy), "
+                      f"{dt:.1f} s, scaled by {R}/{done}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import sparse_attention_fp8_amd as dsa
+    from sparse_attention_fp8_amd import synth
+
+    dsa.load()
+    dev = torch.device("cuda:0")
+    wl = synth.make_config(args.config, args.seed)
+    R, H, k = wl.num_rows, wl.num_heads, wl.topk
+    prefill = wl.max_q_len > 2
+    nbytes = algorithmic_bytes(wl)
+    touched = nbytes["indexer"] + nbytes["sparse_mla"]
+    copies = args.copies or int(min(8, max(2, math.ceil(1.0e9 / max(touched, 1)))))
+
+    batch = dsa.Batch.from_host(wl.seq_lens, wl.query_start, wl.block_table, wl.num_pages, device=dev)
+    sets = []
+    base = {"q_fp8": wl.q_fp8.to(dev), "weights": wl.weights.to(dev), "idx_cache": wl.idx_cache.to(dev),
+            "q_mla": wl.q_mla.to(dev), "kv_cache": wl.kv_cache.to(dev)}
+    sets.append(base)
+    for _ in range(copies - 1):
+        sets.append({n: t.clone() for n, t in base.items()})
+    stride = (wl.max_seq_len + 3) // 4 * 4
+    logits = torch.empty(R, stride, dtype=torch.float32, device=dev)
+    indices = torch.empty(R, k, dtype=torch.int32, device=dev)
+    out = torch.empty(R, H, 512, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(R, H, dtype=torch.float32, device=dev)
+    ws_topk = torch.empty(max(dsa.topk_workspace_bytes(batch, k), 1), dtype=torch.uint8, device=dev)
+    ws_mla = torch.empty(max(dsa.sparse_mla_workspace_bytes(batch, H, k, args.splits), 1), dtype=torch.uint8,
+                         device=dev)
+    splits = args.splits or dsa.sparse_mla_pick_splits(batch, H, k)
+    indexer = dsa.indexer_logits_prefill if prefill else dsa.indexer_logits_paged
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(i, events=None):
+        t = sets[i % copies]
+        if events:
+            events[0].record()
+        indexer(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=False)
+        if events:
+            events[1].record()
+        dsa.topk(batch, logits, indices, k=k, workspace=ws_topk)
+        if events:
+            events[2].record()
+        dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
+                              num_splits=args.splits, workspace=ws_mla)
+        if events:
+            events[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i, ev[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    stage_ms = {
+        "indexer": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+        "topk": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+        "sparse_mla": float(np.mean([e[2].elapsed_time(e[3]) for e in ev])),
+    }
+    total_bytes = nbytes["indexer"] + nbytes["topk"] + nbytes["sparse_mla"]
+    if prefill:
+        dom = "indexer"
+        achieved = nbytes["indexer_flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                "kernel": "indexer_prefill", "per_launch": f"{nbytes['indexer_flops']} flop"}
+    else:
+        dom = max(stage_ms, key=stage_ms.get)
+        achieved = nbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                "per_launch": f"{nbytes[dom]} B"}
+    line = {
+        "metric": "DSA decode steps/s (indexer+topk+sparse MLA) and % of HBM roofline at 1 GPU",
+        "value": 1000.0 / ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 indexer / bf16 MLA, fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": synth.CONFIGS[args.config], "name": args.config, "rows": R, "mla_heads": H,
+                   "topk": k, "splits": splits, "cache_copies": copies, "seed": args.seed or int(args.config[1:])},
+        "roofline": roof,
+        "stages_ms": stage_ms,
+        "step_bytes": total_bytes,
+        "step_hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "rows_per_s": R * 1000.0 / ms,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

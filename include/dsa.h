@@ -1,0 +1,195 @@
+/*
+ * dsa.h -- libdsa: the DeepSeek-Sparse-Attention (DSA) decode hot path on
+ * AMD MI355X (gfx950), behind a plain C ABI.
+ *
+ * One DSA layer step runs three stages for every query row (the vLLM PR page
+ * "[Feature] TRITON_MLA_SPARSE backend for SM8x/11x/12x DSA Sparse MLA
+ * Support", section Changes, items 2 and 3):
+ *   1. lightning-indexer MQA logits over a paged FP8 indexer-K cache
+ *      (dsa_indexer_logits_paged for decode, dsa_indexer_logits_prefill for
+ *      chunked prefill);
+ *   2. per-row top-k of those logits, k = index_topk = 2048 (dsa_topk);
+ *   3. sparse MLA attention over only the selected tokens of a paged bf16
+ *      latent cache, split-KV partials merged by online softmax, with a
+ *      single-pass fast path (dsa_sparse_mla_decode).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers are DEVICE pointers unless the comment says [host].  The caller
+ *    owns every buffer; the library never allocates, frees or keeps device
+ *    memory and keeps no state between calls.  Outputs must not alias inputs.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *    call only enqueues work on it and never synchronises, so a device fault
+ *    surfaces at the caller's next synchronisation.  Launch geometry depends on
+ *    host fields only, so a call can be captured into a HIP graph.
+ *  - Return value: DSA_OK (0) or a negative dsa_status.  Argument checks run on
+ *    the host before anything is launched; on failure nothing is enqueued and
+ *    dsa_last_error_message() (thread-local) says what was wrong.
+ *  - Device contents are validated only where a bad value could make a kernel
+ *    touch memory it does not own: sequence lengths are clamped to max_seq_len,
+ *    query rows to num_rows, block-table entries outside [0, num_pages) mark
+ *    their tokens masked, and top-k indices outside a row's causal range are
+ *    masked, never dereferenced.
+ *
+ * Geometry of a step
+ * ------------------
+ *  Sequence b has L_b = seq_lens[b] cached tokens (this step's queries
+ *  included) and q_len_b = query_start[b+1] - query_start[b] query rows.  Row
+ *  r = query_start[b] + i (0 <= i < q_len_b) sees keys [0, e_r) with
+ *      e_r = L_b - q_len_b + i + 1   (floored at 0)
+ *  -- the per-row causal bound: a decode row sees the whole context, the two
+ *  rows of a draft+verify (MTP) step see L-1 and L keys.
+ *  Logical token s of sequence b lives in physical page
+ *  block_table[b * bt_stride + s / 64], slot s % 64.  Block size is 64 (the
+ *  indexer requires it; the pages' backend declares MultipleOf(64)).  One block
+ *  table serves both caches: the same physical page id indexes the indexer
+ *  cache and the latent cache, each with its own page stride (the KV unifier
+ *  pads indexer pages, vllm-dsa-mtp-sm80 README, skew fix 0).
+ *
+ * Cache layouts
+ * -------------
+ *  Indexer K page (132 bytes per token, 64 tokens): bytes [0, 8192) hold
+ *  [64 tokens][128] OCP e4m3 codes (e4m3fn, max 448), bytes [8192, 8448) hold
+ *  the 64 fp32 per-token scales.  Pages are idx_page_stride bytes apart
+ *  (>= 8448, a multiple of 16; padding is never read).
+ *  Latent page: [64 tokens][576] bf16 (512 latent = V, then 64 rope), pages
+ *  kv_page_stride ELEMENTS apart (>= 64*576, a multiple of 8).
+ */
+#ifndef LIBDSA_DSA_H
+#define LIBDSA_DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL                        */
+  DSA_ERR_INVALID = -2,     /* a size, stride or alignment is out of contract    */
+  DSA_ERR_UNSUPPORTED = -3, /* a valid shape this build has no kernel for       */
+  DSA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
+  DSA_ERR_HIP = -5          /* the HIP runtime rejected a launch                 */
+} dsa_status;
+
+#define DSA_PAGE_SIZE 64
+#define DSA_INDEXER_HEADS 64
+#define DSA_INDEXER_DIM 128
+#define DSA_INDEXER_PAGE_BYTES 8448
+#define DSA_KV_DIM 576
+#define DSA_V_DIM 512
+#define DSA_MAX_TOPK 2048
+#define DSA_MAX_SEQS 4096
+
+/* One step's batch description, shared by all four calls. */
+typedef struct {
+  int32_t num_seqs;            /* B, 0 <= B <= DSA_MAX_SEQS                          [host] */
+  int32_t num_rows;            /* R = total query rows = query_start[B]              [host] */
+  int32_t max_seq_len;         /* >= every L_b; sizes grids and splits, clamps L_b   [host] */
+  int32_t max_q_len;           /* >= every q_len_b (1 decode, 2 MTP, large prefill)  [host] */
+  int32_t bt_stride;           /* block-table row length, >= ceil(max_seq_len / 64)  [host] */
+  int32_t num_pages;           /* physical pages in each cache (ids 0..num_pages-1)  [host] */
+  const int32_t* seq_lens;     /* [B]     L_b                                               */
+  const int32_t* query_start;  /* [B+1]   non-decreasing row offsets, query_start[0] = 0    */
+  const int32_t* block_table;  /* [B, bt_stride] physical page ids                          */
+} dsa_batch_t;
+
+/*
+ * dsa_indexer_logits_paged -- lightning-indexer logits, decode shape.
+ * (PR page, Changes item 2: "paged MQA logits" with in-kernel FP8 decode and
+ * the K-side scale applied to the fp32 dot output.)
+ *
+ *   logits[r, s] = sum_h weights[r, h] * max(q[r, h, :] . k[s, :], 0) * kscale[s]
+ *   for 0 <= s < e_r, with q and k decoded from e4m3, the 128-term dots and the
+ *   64-term head sum accumulated in fp32.
+ *
+ *  q_fp8         [R, 64, 128] e4m3 codes, 16-byte aligned.  Any q scale must be
+ *                folded into `weights` by the caller.
+ *  weights       [R, 64] fp32, 16-byte aligned.
+ *  idx_cache     indexer pages, 16-byte aligned; idx_page_stride in bytes.
+ *  logits        [R, logits_stride] fp32, 16-byte aligned;
+ *                logits_stride >= max_seq_len and a multiple of 4.
+ *  clean_logits  1: columns [e_r, logits_stride) of every row are set to -inf
+ *                ("clean"); 0: they are left untouched ("dirty").  Tokens whose
+ *                block maps outside [0, num_pages) get -inf either way.
+ * Best for max_q_len <= 2 (decode, MTP); correct for any q_len.
+ */
+int dsa_indexer_logits_paged(const dsa_batch_t* batch, const uint8_t* q_fp8, const float* weights,
+                             const uint8_t* idx_cache, int64_t idx_page_stride, float* logits,
+                             int64_t logits_stride, int clean_logits, void* stream);
+
+/*
+ * dsa_indexer_logits_prefill -- the same logits for chunked prefill, where a
+ * sequence has many query rows (PR page, Changes item 2: prefill MQA logits
+ * with a per-row causal bound and a per-row early exit over key tiles).  Same
+ * arguments and result as dsa_indexer_logits_paged; pages are read directly
+ * through the block table, so no gathered copy of K is needed.  Tuned for
+ * q_len_b >> 1 (fp8-MFMA bound); correct for any q_len.
+ */
+int dsa_indexer_logits_prefill(const dsa_batch_t* batch, const uint8_t* q_fp8, const float* weights,
+                               const uint8_t* idx_cache, int64_t idx_page_stride, float* logits,
+                               int64_t logits_stride, int clean_logits, void* stream);
+
+/*
+ * dsa_topk -- indices of the k largest logits[r, 0:e_r) of every row (PR page
+ * review thread: index_topk = 2048 and the exact chunked top-k argument).
+ *  Order of selection: larger value first; equal values (IEEE equality, so -0
+ *  equals +0) go to the lower index.  indices[r, 0:n) = the chosen
+ *  n = min(k, e_r) indices in ascending order, indices[r, n:k) = -1.  Only
+ *  columns [0, e_r) are read.  NaN logits give an unspecified (but in-range)
+ *  selection.
+ *  logits     [R, logits_stride] fp32, 16-byte aligned, logits_stride % 4 == 0
+ *  k          1 <= k <= DSA_MAX_TOPK
+ *  indices    [R, k] int32
+ *  workspace  device scratch of at least dsa_topk_workspace_bytes(batch, k)
+ *             bytes (may be NULL when that is 0); 256-byte aligned.
+ */
+int dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_stride, int32_t k,
+             int32_t* indices, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_decode -- sparse MLA over the selected tokens (PR page,
+ * Changes item 3: split-KV decode with an N-way online-softmax merge, a
+ * single-pass fast path, and -1e30 as the masked sentinel so all-masked tiles
+ * never form (-inf) - (-inf)).  For every row r and head h, over the valid
+ * entries s of indices[r, 0:k) (0 <= s < e_r and on an in-range page; others
+ * are masked; duplicates count as listed):
+ *     z_s = softmax_scale * q[r, h, 0:576] . c_s[0:576]
+ *     out[r, h, :] = sum_s softmax(z)_s * c_s[0:512]      (bf16, round to nearest even)
+ *     lse[r, h]    = ln sum_s exp(z_s)                     (fp32; -inf, out = 0 if none valid)
+ *  q           [R, H, 576] bf16, 16-byte aligned
+ *  num_heads   H: 16, 32, or a multiple of 64
+ *  kv_cache    latent pages, 16-byte aligned; kv_page_stride in elements
+ *  indices     [R, k] int32 logical token ids (typically dsa_topk's output)
+ *  k           1 <= k <= DSA_MAX_TOPK
+ *  num_splits  0 = automatic (dsa_sparse_mla_pick_splits), 1 = single pass,
+ *              n > 1 = the k slots cut into n contiguous ranges merged N-way
+ *              (clamped to the number of 64-slot tiles)
+ *  out         [R, H, 512] bf16;  lse [R, H] fp32 (either may not be NULL)
+ *  workspace   at least dsa_sparse_mla_workspace_bytes(batch, H, k, num_splits)
+ *              bytes, 256-byte aligned (NULL allowed when that is 0)
+ */
+int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads,
+                          const uint16_t* kv_cache, int64_t kv_page_stride, const int32_t* indices,
+                          int32_t k, float softmax_scale, int32_t num_splits, uint16_t* out,
+                          float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace sizes (host fields of `batch` only; 0 when none is needed). */
+size_t dsa_topk_workspace_bytes(const dsa_batch_t* batch, int32_t k);
+size_t dsa_sparse_mla_workspace_bytes(const dsa_batch_t* batch, int32_t num_heads, int32_t k,
+                                      int32_t num_splits);
+/* The split count num_splits = 0 resolves to (depends on host fields only). */
+int32_t dsa_sparse_mla_pick_splits(const dsa_batch_t* batch, int32_t num_heads, int32_t k);
+
+const char* dsa_status_string(int status);
+const char* dsa_last_error_message(void);
+/* "libdsa <version> gfx950" */
+const char* dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDSA_DSA_H */

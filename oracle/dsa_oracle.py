@@ -121,27 +121,27 @@ def indexer_logits(q_fp8, weights, idx_cache, block_table, seq_lens, query_start
     sum_h w[r,h] * max(q_h . k_s, 0) * kscale_s, magnitude[r, s] is the same sum
     with |w[r,h]| (the scale the comparison tolerance is relative to), and
     columns s >= e_r hold -inf when ``clean`` and NaN (meaning: not written)
-    otherwise.  ``rows`` restricts the computation to a subset of rows (the
-    others stay NaN).
+    otherwise.  ``rows`` restricts the computation to the listed rows; the
+    returned arrays then hold just those rows, in that order (e stays full).
     """
     q_fp8 = np.asarray(q_fp8, dtype=np.uint8)
     w = np.asarray(weights, dtype=np.float64)
     bt = np.asarray(block_table, dtype=np.int64)
     seq, ext = row_extents(seq_lens, query_start)
-    R = len(ext)
-    logits = np.full((R, logits_stride), np.nan)
-    mag = np.full((R, logits_stride), np.nan)
+    row_list = list(range(len(ext))) if rows is None else [int(r) for r in rows]
+    logits = np.full((len(row_list), logits_stride), np.nan)
+    mag = np.full((len(row_list), logits_stride), np.nan)
     num_pages = np.asarray(idx_cache).shape[0]
-    for r in (range(R) if rows is None else rows):
+    for o, r in enumerate(row_list):
         e = int(ext[r])
         if clean:
-            logits[r, e:] = -np.inf
+            logits[o, e:] = -np.inf
         if e == 0:
             continue
         page, _ = token_location(bt[seq[r]], np.arange(e))
         ok = (page >= 0) & (page < num_pages)
-        logits[r, :e] = -np.inf                # tokens on an out-of-range page stay masked
-        mag[r, :e] = 0.0
+        logits[o, :e] = -np.inf                # tokens on an out-of-range page stay masked
+        mag[o, :e] = 0.0
         if not ok.any():
             continue
         s = np.nonzero(ok)[0]
@@ -149,8 +149,8 @@ def indexer_logits(q_fp8, weights, idx_cache, block_table, seq_lens, query_start
         Q = e4m3fn_decode(q_fp8[r])            # [64, 128]
         K = e4m3fn_decode(codes)               # [n, 128]
         relu = np.maximum(Q @ K.T, 0.0)        # [64, n]
-        logits[r, s] = (w[r] @ relu) * scales
-        mag[r, s] = (np.abs(w[r]) @ relu) * scales
+        logits[o, s] = (w[r] @ relu) * scales
+        mag[o, s] = (np.abs(w[r]) @ relu) * scales
     return logits, mag, ext
 
 
@@ -170,12 +170,13 @@ def topk_row(values, e, k):
 
 
 def topk(logits, seq_lens, query_start, k, rows=None):
-    """top-k of every row over its own causal extent."""
+    """top-k of every row over its own causal extent.  With ``rows``, logits and
+    the result hold just those rows, in that order."""
     _, ext = row_extents(seq_lens, query_start)
-    R = len(ext)
-    out = np.full((R, int(k)), -1, dtype=np.int64)
-    for r in (range(R) if rows is None else rows):
-        out[r] = topk_row(logits[r], int(ext[r]), k)
+    row_list = list(range(len(ext))) if rows is None else [int(r) for r in rows]
+    out = np.full((len(row_list), int(k)), -1, dtype=np.int64)
+    for o, r in enumerate(row_list):
+        out[o] = topk_row(logits[o], int(ext[r]), k)
     return out
 
 
@@ -208,7 +209,8 @@ def sparse_mla(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
     For each row and head over the row's valid selected latent rows c_j:
     z_j = scale * q . c_j (576 dims); out = sum softmax(z)_j c_j[:512];
     lse = ln sum_j exp(z_j).  A row with no valid entry gives out = 0 and
-    lse = -inf.
+    lse = -inf.  With ``rows``, ``indices`` and the outputs hold just those
+    rows, in that order.
     """
     q_u16 = np.asarray(q_mla)
     R, H, _ = q_u16.shape
@@ -216,10 +218,11 @@ def sparse_mla(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
     if num_pages is None:
         num_pages = int(np.asarray(kv_cache).shape[0])
     seq, ext = row_extents(seq_lens, query_start)
-    out = np.zeros((R, H, V_DIM))
-    lse = np.full((R, H), -np.inf)
-    for r in (range(R) if rows is None else rows):
-        C = _selected_rows(kv_cache, bt[seq[r]], indices[r], int(ext[r]), num_pages)
+    row_list = list(range(R)) if rows is None else [int(r) for r in rows]
+    out = np.zeros((len(row_list), H, V_DIM))
+    lse = np.full((len(row_list), H), -np.inf)
+    for o, r in enumerate(row_list):
+        C = _selected_rows(kv_cache, bt[seq[r]], indices[o], int(ext[r]), num_pages)
         if C.shape[0] == 0:
             continue
         Q = bf16_decode(q_u16[r])                       # [H, 576]
@@ -227,8 +230,8 @@ def sparse_mla(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
         M = z.max(axis=1, keepdims=True)
         p = np.exp(z - M)
         l = p.sum(axis=1, keepdims=True)
-        out[r] = (p @ C[:, :V_DIM]) / l
-        lse[r] = (M + np.log(l))[:, 0]
+        out[o] = (p @ C[:, :V_DIM]) / l
+        lse[o] = (M + np.log(l))[:, 0]
     return out, lse
 
 
@@ -253,13 +256,14 @@ def sparse_mla_split(q_mla, kv_cache, block_table, seq_lens, query_start, indice
         num_pages = int(np.asarray(kv_cache).shape[0])
     seq, ext = row_extents(seq_lens, query_start)
     per = -(-k // num_splits)
-    out = np.zeros((R, H, V_DIM))
-    lse = np.full((R, H), -np.inf)
-    for r in (range(R) if rows is None else rows):
+    row_list = list(range(R)) if rows is None else [int(r) for r in rows]
+    out = np.zeros((len(row_list), H, V_DIM))
+    lse = np.full((len(row_list), H), -np.inf)
+    for o, r in enumerate(row_list):
         Q = bf16_decode(q_u16[r])
         ms, ls, accs = [], [], []
         for i in range(num_splits):
-            C = _selected_rows(kv_cache, bt[seq[r]], idx[r, i * per:(i + 1) * per],
+            C = _selected_rows(kv_cache, bt[seq[r]], idx[o, i * per:(i + 1) * per],
                                int(ext[r]), num_pages)
             m = np.full(H, MASK_SENTINEL)
             l = np.zeros(H)
@@ -278,6 +282,6 @@ def sparse_mla_split(q_mla, kv_cache, block_table, seq_lens, query_start, indice
         L = sum(l * wt for l, wt in zip(ls, wts))
         A = sum(a * wt[:, None] for a, wt in zip(accs, wts))
         ok = L > 0
-        out[r][ok] = A[ok] / L[ok][:, None]
-        lse[r][ok] = M[ok] + np.log(L[ok])
+        out[o][ok] = A[ok] / L[ok][:, None]
+        lse[o][ok] = M[ok] + np.log(L[ok])
     return out, lse

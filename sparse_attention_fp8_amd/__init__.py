@@ -1,0 +1,11 @@
+"""libdsa: DeepSeek-Sparse-Attention decode hot path for MI355X (gfx950).
+
+The compute is in hand-written HIP kernels behind the C ABI of
+``include/dsa.h``; this package is only the Python binding (argument
+marshalling through ctypes) plus the synthetic-workload generator.
+"""
+from .binding import (  # noqa: F401
+    DSAError, load, library_path, indexer_logits_paged, indexer_logits_prefill, topk,
+    sparse_mla_decode, topk_workspace_bytes, sparse_mla_workspace_bytes, sparse_mla_pick_splits,
+    Batch,
+)

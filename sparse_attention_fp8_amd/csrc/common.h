@@ -1,0 +1,100 @@
+// Device-side helpers shared by the libdsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+constexpr int kPage = DSA_PAGE_SIZE;            // tokens per block
+constexpr int kIdxHeads = DSA_INDEXER_HEADS;    // 64
+constexpr int kIdxDim = DSA_INDEXER_DIM;        // 128
+constexpr int kIdxScaleOff = kPage * kIdxDim;   // 8192: scales follow the codes
+constexpr int kKvDim = DSA_KV_DIM;              // 576
+constexpr int kVDim = DSA_V_DIM;                // 512
+constexpr float kMaskSentinel = -1e30f;         // running-max start of masked tiles
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// The host-visible batch fields the kernels need, passed by value.
+struct BatchArgs {
+  int num_seqs, num_rows, max_seq_len, max_q_len, bt_stride, num_pages;
+  const int* seq_lens;
+  const int* query_start;
+  const int* block_table;
+};
+
+__device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
+
+// Row r's sequence: the b with query_start[b] <= r < query_start[b+1] (binary
+// search; query_start is non-decreasing).  Returns -1 when r lies outside.
+__device__ __forceinline__ int seq_of_row(const int* qs, int num_seqs, int r) {
+  int lo = 0, hi = num_seqs;  // answer in [lo, hi)
+  if (num_seqs <= 0 || r < qs[0] || r >= qs[num_seqs]) return -1;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (qs[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Causal extent of row r of sequence b: e_r = L_b - q_len_b + i + 1, in [0, L_b].
+__device__ __forceinline__ int row_extent(const BatchArgs& a, int b, int r) {
+  const int q0 = a.query_start[b], q1 = a.query_start[b + 1];
+  const int L = clamp_len(a.seq_lens[b], a.max_seq_len);
+  const int e = L - (q1 - q0) + (r - q0) + 1;
+  return e < 0 ? 0 : (e > L ? L : e);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key), with -0
+// folded onto +0 so the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// bf16 helpers (bit patterns in uint16 / packed pairs in uint32).
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+}  // namespace dsa

@@ -1,0 +1,169 @@
+"""Host-side tests of the C ABI: the library loads, exports every declared
+symbol, and rejects out-of-contract arguments before launching anything.
+
+No GPU is touched: every call here fails validation (or is a pure host query),
+so the pointers passed are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_fp8_amd as dsa
+from sparse_attention_fp8_amd.binding import _Batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, ERR_NULL, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE = 0, -1, -2, -3, -4
+FAKE = 0x10000  # a 256-byte aligned non-NULL address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int32_t|size_t|int)\s+(dsa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dsa.load()
+
+
+def batch(**kw):
+    f = dict(num_seqs=2, num_rows=3, max_seq_len=5000, max_q_len=2, bt_stride=79, num_pages=200,
+             seq_lens=FAKE, query_start=FAKE, block_table=FAKE)
+    f.update(kw)
+    return _Batch(**f)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"dsa_indexer_logits_paged", "dsa_indexer_logits_prefill", "dsa_topk",
+            "dsa_sparse_mla_decode"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.dsa_version()
+    for st in (OK, ERR_NULL, ERR_INVALID, ERR_UNSUPPORTED, ERR_WORKSPACE, -5):
+        assert lib.dsa_status_string(st)
+    assert lib.dsa_status_string(42) == b"unknown dsa_status"
+
+
+def idx_call(lib, fn, b, **kw):
+    a = dict(q=FAKE, w=FAKE, cache=FAKE, page_stride=8448, logits=FAKE, logits_stride=5000, clean=1)
+    a.update(kw)
+    f = getattr(lib, fn)
+    bp = None if b is None else ctypes.byref(b)
+    return f(bp, a["q"], a["w"], a["cache"], a["page_stride"], a["logits"], a["logits_stride"], a["clean"], None)
+
+
+@pytest.mark.parametrize("fn", ["dsa_indexer_logits_paged", "dsa_indexer_logits_prefill"])
+def test_indexer_argument_checks(lib, fn):
+    assert idx_call(lib, fn, None) == ERR_NULL
+    assert idx_call(lib, fn, batch(num_seqs=-1)) == ERR_UNSUPPORTED
+    assert idx_call(lib, fn, batch(num_seqs=4097)) == ERR_UNSUPPORTED
+    assert idx_call(lib, fn, batch(num_rows=-2)) == ERR_INVALID
+    assert idx_call(lib, fn, batch(bt_stride=78)) == ERR_INVALID          # < ceil(5000/64) = 79
+    assert idx_call(lib, fn, batch(seq_lens=None)) == ERR_NULL
+    assert idx_call(lib, fn, batch(block_table=None)) == ERR_NULL
+    assert idx_call(lib, fn, batch(), page_stride=8447) == ERR_INVALID
+    assert idx_call(lib, fn, batch(), page_stride=8456) == ERR_INVALID     # not a multiple of 16
+    assert idx_call(lib, fn, batch(), logits_stride=4999) == ERR_INVALID   # < max_seq_len
+    assert idx_call(lib, fn, batch(), logits_stride=5002) == ERR_INVALID   # not a multiple of 4
+    assert idx_call(lib, fn, batch(), clean=2) == ERR_INVALID
+    assert idx_call(lib, fn, batch(), q=None) == ERR_NULL
+    assert idx_call(lib, fn, batch(), logits=FAKE + 4) == ERR_INVALID      # misaligned
+    assert idx_call(lib, fn, batch(), cache=None) == ERR_NULL
+    idx_call(lib, fn, batch(), page_stride=100)
+    assert b"idx_page_stride" in lib.dsa_last_error_message()
+    # nothing to do is a success that launches nothing
+    assert idx_call(lib, fn, batch(num_rows=0)) == OK
+
+
+def topk_call(lib, b, k=2048, ws=FAKE, ws_bytes=1 << 40, **kw):
+    a = dict(logits=FAKE, stride=5000, indices=FAKE)
+    a.update(kw)
+    return lib.dsa_topk(None if b is None else ctypes.byref(b), a["logits"], a["stride"], k, a["indices"],
+                        ws, ws_bytes, None)
+
+
+def test_topk_argument_checks(lib):
+    assert topk_call(lib, None) == ERR_NULL
+    assert topk_call(lib, batch(), k=0) == ERR_UNSUPPORTED
+    assert topk_call(lib, batch(), k=2049) == ERR_UNSUPPORTED
+    assert topk_call(lib, batch(), stride=4000) == ERR_INVALID
+    assert topk_call(lib, batch(), logits=None) == ERR_NULL
+    assert topk_call(lib, batch(), indices=None) == ERR_NULL
+    assert topk_call(lib, batch(), logits=FAKE + 8) == ERR_INVALID
+    long = batch(max_seq_len=131072, bt_stride=2048)
+    need = lib.dsa_topk_workspace_bytes(ctypes.byref(long), 2048)
+    assert need > 0
+    assert topk_call(lib, long, stride=131072, ws=None) == ERR_WORKSPACE
+    assert topk_call(lib, long, stride=131072, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert topk_call(lib, long, stride=131072, ws=FAKE + 16) == ERR_INVALID
+    assert b"workspace" in lib.dsa_last_error_message()
+
+
+def test_topk_workspace_sizes(lib):
+    # rows that fit one 16384-key chunk need no workspace
+    assert lib.dsa_topk_workspace_bytes(ctypes.byref(batch(max_seq_len=16384, bt_stride=256)), 2048) == 0
+    b = batch(max_seq_len=65536, bt_stride=1024, num_rows=4096)
+    need = lib.dsa_topk_workspace_bytes(ctypes.byref(b), 2048)
+    assert need >= 4096 * 4 * 2048 * 8 and need % 256 == 0
+    assert lib.dsa_topk_workspace_bytes(None, 2048) == 0
+
+
+def mla_call(lib, b, H=16, k=2048, splits=0, ws=FAKE, ws_bytes=1 << 40, **kw):
+    a = dict(q=FAKE, kv=FAKE, kv_stride=64 * 576, indices=FAKE, scale=0.07, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return lib.dsa_sparse_mla_decode(None if b is None else ctypes.byref(b), a["q"], H, a["kv"], a["kv_stride"],
+                                     a["indices"], k, a["scale"], splits, a["out"], a["lse"], ws, ws_bytes, None)
+
+
+def test_sparse_mla_argument_checks(lib):
+    assert mla_call(lib, None) == ERR_NULL
+    for H in (0, 8, 48, 96, 100):
+        assert mla_call(lib, batch(), H=H) == ERR_UNSUPPORTED, H
+    assert mla_call(lib, batch(), k=0) == ERR_UNSUPPORTED
+    assert mla_call(lib, batch(), k=4096) == ERR_UNSUPPORTED
+    assert mla_call(lib, batch(), kv_stride=64 * 576 - 8) == ERR_INVALID
+    assert mla_call(lib, batch(), kv_stride=64 * 576 + 4) == ERR_INVALID
+    assert mla_call(lib, batch(), scale=float("inf")) == ERR_INVALID
+    assert mla_call(lib, batch(), splits=-1) == ERR_INVALID
+    assert mla_call(lib, batch(), out=None) == ERR_NULL
+    assert mla_call(lib, batch(), lse=None) == ERR_NULL
+    assert mla_call(lib, batch(), q=FAKE + 2) == ERR_INVALID
+    assert mla_call(lib, batch(), kv=None) == ERR_NULL
+    b = batch(num_rows=1)
+    need = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(b), 16, 2048, 0)
+    assert need > 0
+    assert mla_call(lib, b, ws=None) == ERR_WORKSPACE
+    assert mla_call(lib, b, ws_bytes=need - 1) == ERR_WORKSPACE
+
+
+def test_split_heuristic_and_workspace(lib):
+    def splits(R, L, H):
+        return lib.dsa_sparse_mla_pick_splits(ctypes.byref(batch(num_rows=R, max_seq_len=L, bt_stride=(L + 63) // 64)), H, 2048)
+    assert splits(1, 131072, 16) >= 16          # single long row: many splits
+    assert splits(1, 4096, 16) >= 16
+    assert splits(4096, 65536, 16) == 1         # prefill-sized batch: single pass
+    assert splits(1, 100, 16) == 2              # never more splits than tiles holding keys
+    assert 1 <= splits(128, 65536, 128) <= 4
+    # one split needs no workspace
+    b = batch(num_rows=4096, max_seq_len=65536, bt_stride=1024)
+    assert lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(b), 16, 2048, 1) == 0
+    b = batch(num_rows=2, max_seq_len=5000, bt_stride=79)
+    ws = lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(b), 32, 2048, 4)
+    assert ws >= 4 * 2 * 32 * (512 * 4 + 8)
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    b = dsa.Batch(seq_lens=torch.zeros(1, dtype=torch.int32), query_start=torch.zeros(2, dtype=torch.int32),
+                  block_table=torch.zeros(1, 1, dtype=torch.int32), num_rows=0, max_seq_len=0, max_q_len=0,
+                  num_pages=1)
+    with pytest.raises(ValueError):
+        b.c_struct()

@@ -1,0 +1,324 @@
+"""GPU parity of every libdsa entry point against the float64 oracle.
+
+Sizes are small enough for the oracle to finish in seconds but span several
+tiles, ragged page tails, multi-chunk top-k rows and every split mode.  Caches
+are poisoned (NaN codes / scales / bf16) outside the live tokens, so any read
+of an unreferenced slot shows up.  Tolerances:
+  indexer logits   |gpu - oracle| <= 1e-3 * sum_h |w_h| relu(dot_h) kscale   (the
+                   magnitude the signed 64-head sum is made of; -inf masks equal)
+  top-k            bit-exact vs a CPU selection over the GPU's own logits
+  sparse MLA out   max-abs <= 2e-2, mean-abs <= 2e-3 vs the oracle's float64
+                   (pre-rounding) value; lse abs <= 1e-3
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_fp8_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+LOGIT_TOL = 1e-3
+OUT_MAX, OUT_MEAN, LSE_TOL = 2e-2, 2e-3, 1e-3
+
+
+def to_dev(wl):
+    import sparse_attention_fp8_amd as dsa
+    batch = dsa.Batch.from_host(wl.seq_lens, wl.query_start, wl.block_table, wl.num_pages, device=DEV)
+    return batch, {"q_fp8": wl.q_fp8.to(DEV), "weights": wl.weights.to(DEV), "idx_cache": wl.idx_cache.to(DEV),
+                   "q_mla": wl.q_mla.to(DEV), "kv_cache": wl.kv_cache.to(DEV)}
+
+
+def run_indexer(dsa, wl, batch, t, stride, clean=True, prefill=False, fill=float("nan")):
+    logits = torch.full((wl.num_rows, stride), fill, dtype=torch.float32, device=DEV)
+    fn = dsa.indexer_logits_prefill if prefill else dsa.indexer_logits_paged
+    fn(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=clean)
+    torch.cuda.synchronize()
+    return logits
+
+
+def oracle_indexer(wl, stride, clean=True, rows=None):
+    return oracle.indexer_logits(wl.q_fp8.numpy(), wl.weights.numpy(), wl.idx_cache.numpy(),
+                                 wl.block_table.numpy(), wl.seq_lens.numpy(), wl.query_start.numpy(),
+                                 stride, clean=clean, rows=rows)
+
+
+def check_logits(got, ref, mag, what=""):
+    got = np.asarray(got, np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: -inf pattern differs"
+    fin = np.isfinite(ref)
+    assert np.isfinite(got[fin]).all(), f"{what}: non-finite logits where the oracle is finite"
+    err = np.abs(got[fin] - ref[fin])
+    bound = LOGIT_TOL * mag[fin]
+    bad = err > bound
+    assert not bad.any(), f"{what}: {bad.sum()} logits out of tolerance, worst ratio {(err / np.maximum(bound, 1e-300)).max():.3g}"
+
+
+def mla_oracle(wl, idx, rows=None):
+    return oracle.sparse_mla(wl.q_mla.view(torch.int16).numpy(), wl.kv_cache.view(torch.int16).numpy(),
+                             wl.block_table.numpy(), wl.seq_lens.numpy(), wl.query_start.numpy(), idx,
+                             wl.softmax_scale, num_pages=wl.num_pages, rows=rows)
+
+
+def check_mla(out, lse, o_ref, l_ref, what=""):
+    o = out.float().cpu().numpy().astype(np.float64)
+    ls = lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    d = np.abs(o - o_ref)
+    assert d.max() <= OUT_MAX and d.mean() <= OUT_MEAN, f"{what}: out max {d.max():.3g} mean {d.mean():.3g}"
+    assert np.array_equal(np.isneginf(ls), np.isneginf(l_ref)), f"{what}: -inf lse pattern differs"
+    fin = np.isfinite(l_ref)
+    if fin.any():
+        assert np.abs(ls[fin] - l_ref[fin]).max() <= LSE_TOL, f"{what}: lse err {np.abs(ls[fin] - l_ref[fin]).max():.3g}"
+
+
+# --------------------------------------------------------------------------
+# indexer logits
+
+INDEXER_CASES = {
+    "decode_edges": ([1, 63, 64, 65, 130, 2047, 2048, 2049], [1] * 8, {}),
+    "mtp_pairs": ([3000, 700, 64, 2], [2, 2, 2, 2], {}),
+    "qlen_ge_len": ([5, 300, 3], [5, 3, 7], {}),
+    "padded_pages": ([1000, 333], [1, 3], {"idx_page_pad": 512}),
+    "prefill_rows": ([2600], [200], {}),
+    "many_seqs": (list(range(1, 400, 7)), [1] * 57, {}),
+}
+
+
+@pytest.mark.parametrize("prefill", [False, True], ids=["paged", "prefill"])
+@pytest.mark.parametrize("case", list(INDEXER_CASES))
+def test_indexer_parity(dsa, case, prefill):
+    seq_lens, q_lens, kw = INDEXER_CASES[case]
+    wl = synth.make_workload(seq_lens, q_lens, 16, seed=101, spare_pages=5, poison=True, **kw)
+    batch, t = to_dev(wl)
+    stride = (wl.max_seq_len + 3) // 4 * 4 + 8
+    got = run_indexer(dsa, wl, batch, t, stride, clean=True, prefill=prefill).cpu().numpy()
+    ref, mag, _ = oracle_indexer(wl, stride, clean=True)
+    check_logits(got, ref, mag, f"{case}/{'prefill' if prefill else 'paged'}")
+
+
+@pytest.mark.parametrize("prefill", [False, True], ids=["paged", "prefill"])
+def test_indexer_dirty_leaves_tail(dsa, prefill):
+    wl = synth.make_workload([777, 64, 1], [2, 1, 1], 16, seed=5, spare_pages=2, poison=True)
+    batch, t = to_dev(wl)
+    stride = 1024
+    got = run_indexer(dsa, wl, batch, t, stride, clean=False, prefill=prefill, fill=12345.0).cpu().numpy()
+    ref, mag, ext = oracle_indexer(wl, stride, clean=False)
+    for r, e in enumerate(ext):
+        assert np.all(got[r, e:] == 12345.0), f"row {r}: dirty tail was written"
+    fin = np.isfinite(ref)
+    assert np.all(np.abs(got[fin] - ref[fin]) <= LOGIT_TOL * mag[fin])
+
+
+def test_indexer_all_fp8_codes_decode_exactly(dsa):
+    """Two heads with weights +1/-1 and q = +e_d / -e_d give logit = k_d * scale
+    exactly, so every finite e4m3 byte is checked through the MFMA decode."""
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    L = 256
+    wl = synth.make_workload([L], [1], 16, seed=3, spare_pages=1)
+    rng = np.random.default_rng(0)
+    cache = wl.idx_cache.numpy().copy()
+    bt = wl.block_table.numpy()
+    codes = np.zeros((L, 128), np.uint8)
+    for d in range(128):
+        codes[:, d] = np.concatenate([rng.permutation(finite), finite[:2]])
+    scales = rng.uniform(0.25, 4.0, size=L).astype(np.float32)
+    for s in range(L):
+        p, slot = bt[0, s // 64], s % 64
+        cache[p, slot * 128:(slot + 1) * 128] = codes[s]
+        cache[p, 8192 + 4 * slot:8192 + 4 * slot + 4] = scales[s:s + 1].view(np.uint8)
+    wl.idx_cache = torch.from_numpy(cache)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for d in (0, 1, 31, 64, 127):
+        q = np.zeros((1, 64, 128), np.uint8)
+        w = np.zeros((1, 64), np.float32)
+        q[0, 3, d], w[0, 3] = 0x38, 1.0
+        q[0, 40, d], w[0, 40] = 0xB8, -1.0
+        wl.q_fp8, wl.weights = torch.from_numpy(q), torch.from_numpy(w)
+        batch, t = to_dev(wl)
+        got = run_indexer(dsa, wl, batch, t, L).cpu().numpy()[0]
+        want = (dec[:, d] * scales.astype(np.float64)).astype(np.float32)
+        assert np.array_equal(got, want), f"dim {d}: {np.nonzero(got != want)[0][:8]}"
+
+
+def test_indexer_out_of_range_pages_are_masked(dsa):
+    wl = synth.make_workload([300, 200], [1, 1], 16, seed=9, spare_pages=2)
+    bt = wl.block_table.clone()
+    bt[0, 1] = wl.num_pages + 5     # a bad id inside sequence 0
+    bt[1, 0] = -3
+    wl.block_table = bt
+    batch, t = to_dev(wl)
+    got = run_indexer(dsa, wl, batch, t, 304).cpu().numpy()
+    ref, mag, _ = oracle_indexer(wl, 304)
+    check_logits(got, ref, mag, "bad pages")
+    assert np.all(np.isneginf(got[0, 64:128])) and np.all(np.isneginf(got[1, :64]))
+
+
+# --------------------------------------------------------------------------
+# top-k
+
+def run_topk(dsa, batch, logits, k=2048):
+    idx = torch.full((logits.shape[0], k), -7, dtype=torch.int32, device=DEV)
+    dsa.topk(batch, logits, idx, k=k)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def check_topk(got, logits_np, wl, k):
+    ref = oracle.topk(logits_np, wl.seq_lens.numpy(), wl.query_start.numpy(), k)
+    for r in range(ref.shape[0]):
+        assert np.array_equal(got[r], ref[r]), f"row {r}: first diff at {np.nonzero(got[r] != ref[r])[0][:5]}"
+
+
+@pytest.mark.parametrize("k", [2048, 1, 100, 2047])
+def test_topk_on_indexer_logits(dsa, k):
+    wl = synth.make_workload([1, 2047, 2048, 2049, 5000, 16384, 16385, 40000], [1] * 8, 16, seed=17, spare_pages=3)
+    batch, t = to_dev(wl)
+    stride = 40000
+    logits = run_indexer(dsa, wl, batch, t, stride)
+    got = run_topk(dsa, batch, logits, k)
+    check_topk(got, logits.cpu().numpy(), wl, k)
+
+
+@pytest.mark.parametrize("pool", ["small_set", "signed_zero", "constant"])
+def test_topk_forced_ties(dsa, pool):
+    """Logits drawn from a tiny value set: most of the selection is decided by the
+    lower-index tie rule; rows span one and several chunks."""
+    lens = [10, 2048, 3000, 16384, 17000, 50000]
+    wl = synth.make_workload(lens, [1] * len(lens), 16, seed=23, spare_pages=2)
+    batch, _ = to_dev(wl)
+    rng = np.random.default_rng(1)
+    vals = {"small_set": np.array([-1.0, 0.0, 1.0, 2.0, 2.5], np.float32),
+            "signed_zero": np.array([-0.0, 0.0, -1.0], np.float32),
+            "constant": np.array([3.25], np.float32)}[pool]
+    host = rng.choice(vals, size=(len(lens), 50000)).astype(np.float32)
+    logits = torch.from_numpy(host).to(DEV)
+    got = run_topk(dsa, batch, logits)
+    check_topk(got, host, wl, 2048)
+
+
+def test_topk_ties_from_duplicated_pages(dsa):
+    """Every logical block of a sequence maps to the same physical page, so the
+    logits repeat every 64 keys: ties broken only by index."""
+    wl = synth.make_workload([20000, 3000], [1, 1], 16, seed=29, spare_pages=2)
+    bt = wl.block_table.clone()
+    bt[0, :] = bt[0, 0]
+    bt[1, :] = bt[1, 3]
+    wl.block_table = bt
+    batch, t = to_dev(wl)
+    logits = run_indexer(dsa, wl, batch, t, 20000)
+    h = logits.cpu().numpy()
+    assert np.array_equal(h[0, :64], h[0, 64:128])
+    got = run_topk(dsa, batch, logits)
+    check_topk(got, h, wl, 2048)
+
+
+# --------------------------------------------------------------------------
+# sparse MLA
+
+def mla_inputs(dsa, seq_lens, q_lens, H, seed, k=2048):
+    wl = synth.make_workload(seq_lens, q_lens, H, seed=seed, spare_pages=4, poison=True)
+    batch, t = to_dev(wl)
+    seq, ext = oracle.row_extents(wl.seq_lens.numpy(), wl.query_start.numpy())
+    rng = np.random.default_rng(seed)
+    idx = np.stack([oracle.topk_row(rng.normal(size=max(int(e), 1)), int(e), k) for e in ext])
+    return wl, batch, t, idx
+
+
+def run_mla(dsa, wl, batch, t, idx, splits):
+    R, H = wl.num_rows, wl.num_heads
+    out = torch.full((R, H, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((R, H), float("nan"), dtype=torch.float32, device=DEV)
+    dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], torch.from_numpy(idx.astype(np.int32)).to(DEV),
+                          wl.softmax_scale, out, lse, num_splits=splits)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 16, 32])
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
+def test_sparse_mla_parity(dsa, H, splits):
+    wl, batch, t, idx = mla_inputs(dsa, [3000, 700, 130, 2049], [1, 2, 1, 1], H, seed=H + splits)
+    out, lse = run_mla(dsa, wl, batch, t, idx, splits)
+    o_ref, l_ref = mla_oracle(wl, idx)
+    check_mla(out, lse, o_ref, l_ref, f"H={H} splits={splits}")
+
+
+def test_sparse_mla_masked_duplicate_and_invalid_entries(dsa):
+    wl, batch, t, idx = mla_inputs(dsa, [5000, 600], [1, 2], 16, seed=77)
+    idx = idx.copy()
+    idx[0, 10:20] = idx[0, 0]            # duplicates count as listed
+    idx[0, 100:400] = -1                 # masked stretch
+    idx[1, 5] = 599                      # row 1 sees [0, 599): 599 is out of range
+    idx[2, 7] = 10 ** 6
+    idx[2, 8] = -42
+    for splits in (1, 0, 7):
+        out, lse = run_mla(dsa, wl, batch, t, idx, splits)
+        o_ref, l_ref = mla_oracle(wl, idx)
+        check_mla(out, lse, o_ref, l_ref, f"splits={splits}")
+
+
+def test_sparse_mla_empty_rows(dsa):
+    wl, batch, t, idx = mla_inputs(dsa, [300, 2000], [1, 1], 32, seed=5)
+    idx = idx.copy()
+    idx[0, :] = -1
+    for splits in (1, 4):
+        out, lse = run_mla(dsa, wl, batch, t, idx, splits)
+        assert torch.all(out[0] == 0) and torch.all(torch.isneginf(lse[0]))
+        o_ref, l_ref = mla_oracle(wl, idx)
+        check_mla(out, lse, o_ref, l_ref, f"splits={splits}")
+
+
+def test_sparse_mla_split_matches_single_pass(dsa):
+    wl, batch, t, idx = mla_inputs(dsa, [9000, 4000, 2500], [1, 1, 2], 64, seed=8)
+    o1, l1 = run_mla(dsa, wl, batch, t, idx, 1)
+    for s in (2, 5, 32):
+        o2, l2 = run_mla(dsa, wl, batch, t, idx, s)
+        d = (o1.float() - o2.float()).abs()
+        assert d.max().item() <= 1.6e-2 and d.mean().item() <= 1e-3, s
+        assert (l1 - l2).abs().max().item() <= 1e-4, s
+
+
+def test_page_permutation_invariance_gpu(dsa):
+    """Moving every physical page and rewriting the block table leaves all three
+    stages bit-identical."""
+    wl = synth.make_workload([4000, 2100, 90], [1, 2, 1], 16, seed=31, spare_pages=6)
+    perm = torch.randperm(wl.num_pages, generator=torch.Generator().manual_seed(3))
+    wl2 = synth.make_workload([4000, 2100, 90], [1, 2, 1], 16, seed=31, spare_pages=6)
+    wl2.idx_cache = torch.empty_like(wl.idx_cache)
+    wl2.idx_cache[perm] = wl.idx_cache
+    wl2.kv_cache = torch.empty_like(wl.kv_cache)
+    wl2.kv_cache[perm] = wl.kv_cache
+    wl2.block_table = perm[wl.block_table.long()].to(torch.int32)
+    res = []
+    for w in (wl, wl2):
+        batch, t = to_dev(w)
+        logits = run_indexer(dsa, w, batch, t, 4000)
+        idx = torch.from_numpy(run_topk(dsa, batch, logits)).to(DEV)
+        out = torch.empty(w.num_rows, 16, 512, dtype=torch.bfloat16, device=DEV)
+        lse = torch.empty(w.num_rows, 16, device=DEV)
+        dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], idx, w.softmax_scale, out, lse)
+        torch.cuda.synchronize()
+        res.append((logits.cpu(), idx.cpu(), out.cpu(), lse.cpu()))
+    for a, b in zip(*res):
+        assert torch.equal(a.view(torch.uint8) if a.dtype != torch.int32 else a,
+                           b.view(torch.uint8) if b.dtype != torch.int32 else b)
+
+
+def test_full_step_small(dsa):
+    """indexer -> top-k -> sparse MLA chained on the GPU, each checked."""
+    wl = synth.make_workload([2500, 130, 7000], [2, 1, 1], 16, seed=7, spare_pages=4, poison=True)
+    batch, t = to_dev(wl)
+    stride = 7000
+    logits = run_indexer(dsa, wl, batch, t, stride)
+    ref, mag, _ = oracle_indexer(wl, stride)
+    check_logits(logits.cpu().numpy(), ref, mag, "step")
+    idx = run_topk(dsa, batch, logits)
+    check_topk(idx, logits.cpu().numpy(), wl, 2048)
+    out, lse = run_mla(dsa, wl, batch, t, idx, 0)
+    o_ref, l_ref = mla_oracle(wl, idx)
+    check_mla(out, lse, o_ref, l_ref, "step")
