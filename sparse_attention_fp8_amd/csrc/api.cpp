@@ -153,6 +153,9 @@ int dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_strid
   if (logits_stride < batch->max_seq_len || logits_stride < 1 || logits_stride % 4 != 0)
     return fail(DSA_ERR_INVALID, "logits_stride=%lld must be >= max_seq_len=%d, >= 1 and a multiple of 4",
                 (long long)logits_stride, batch->max_seq_len);
+  if ((int64_t)batch->max_seq_len > dsa::topk_max_seq_len(k))
+    return fail(DSA_ERR_UNSUPPORTED, "max_seq_len=%d exceeds the %lld keys per row dsa_topk handles for k=%d",
+                batch->max_seq_len, (long long)dsa::topk_max_seq_len(k), k);
   if (batch->num_rows == 0) return ok();
   if (!logits || !indices) return fail(DSA_ERR_NULL, "logits and indices must not be NULL");
   if (!aligned(logits, 16)) return fail(DSA_ERR_INVALID, "logits must be 16-byte aligned");

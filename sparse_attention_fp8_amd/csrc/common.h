@@ -69,7 +69,17 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = lane_id();
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    int t = __shfl_up(v, off, 64);
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_inclusive_scan_u64(uint64_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t t = __shfl_up(v, off, 64);
     if (lane >= off) v += t;
   }
   return v;

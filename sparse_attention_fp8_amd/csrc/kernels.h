@@ -20,6 +20,7 @@ hipError_t launch_indexer_prefill(const BatchArgs& batch, const uint8_t* q, cons
                                   int64_t logits_stride, int clean, int num_cus, hipStream_t stream);
 
 int topk_num_chunks(int max_seq_len);
+int64_t topk_max_seq_len(int k);  // longest row one dsa_topk call handles
 size_t topk_workspace_bytes(int num_rows, int max_seq_len, int k);
 hipError_t launch_topk(const BatchArgs& batch, const float* logits, int64_t logits_stride, int k,
                        int32_t* indices, void* workspace, hipStream_t stream);

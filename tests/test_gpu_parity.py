@@ -201,6 +201,23 @@ def test_topk_forced_ties(dsa, pool):
     check_topk(got, host, wl, 2048)
 
 
+@pytest.mark.parametrize("L", [600_000, 140_000])
+def test_topk_long_rows_merge(dsa, L):
+    """Rows far past one 32768-key chunk: many chunks feed the candidate merge
+    (for 600k keys it holds over 32768 candidates); values repeat heavily."""
+    import sparse_attention_fp8_amd as lib
+    lens = [L, L - 1000, 5000]
+    qs = [0, 1, 2, 3]
+    batch = lib.Batch.from_host(lens, qs, np.zeros((3, (L + 63) // 64), np.int32), 1, device=DEV)
+    rng = np.random.default_rng(L)
+    host = np.round(rng.normal(size=(3, L)) * 4.0).astype(np.float32)   # ~30 distinct values
+    host[1, ::7] = host[1, 0]
+    logits = torch.from_numpy(host).to(DEV)
+    got = run_topk(dsa, batch, logits)
+    ref = oracle.topk(host, np.array(lens), np.array(qs), 2048)
+    assert np.array_equal(got, ref)
+
+
 def test_topk_ties_from_duplicated_pages(dsa):
     """Every logical block of a sequence maps to the same physical page, so the
     logits repeat every 64 keys: ties broken only by index."""
