@@ -9,28 +9,33 @@
 // all-masked tile never computes (-inf) - (-inf).
 //
 // gfx950 design.
-//  * Workgroup = 4 waves = one (row, split, block of 16 or 32 heads).  Its
-//    k-slot range is walked in tiles of 64 selected tokens.
-//  * Gather: the 64 selected latent rows (64 x 1152 B) are copied from HBM
-//    straight into LDS with global_load_lds_dwordx4 (no VGPR round trip).  Each
-//    lane supplies its own source address, so the gather through the block
-//    table costs nothing extra; masked slots read a static zero row.  Rows are
-//    padded to 73 sixteen-byte chunks (1168 B): an odd chunk count puts the 16
-//    token rows one MFMA operand read touches on distinct LDS banks, and every
-//    operand address stays "lane base + immediate".
+//  * Workgroup = one (row, split, head block).  Head block and wave roles:
+//      16 heads:  4 waves, each scores 16 of the tile's 64 tokens and
+//                 accumulates 128 of the 512 output dims;
+//      32 heads:  4 waves = 2 head tiles x 2 parts (32 tokens / 256 dims each);
+//      >=64 heads: 8 waves = 4 head tiles x 2 parts, 64-head blocks.
+//    Scores of a head tile are computed once; the tile maximum and the bf16
+//    probabilities are exchanged through LDS between the waves of that head
+//    tile, and every wave accumulates its own dims over all 64 tokens.
+//  * Gather: the 64 selected latent rows of a tile (64 x 1152 B) are copied
+//    from HBM straight into LDS with global_load_lds_dwordx4, double-buffered:
+//    tile i+1 is in flight while tile i is multiplied.  Each lane supplies its
+//    own source address, so the gather through the block table costs nothing
+//    extra; masked slots read a static zero row.  Rows are padded to 73
+//    sixteen-byte chunks (1168 B): an odd chunk count puts the 16 token rows an
+//    MFMA operand read touches on distinct LDS banks, and every operand address
+//    stays "lane base + immediate".
+//  * Row pointers are prepared two tiles ahead by wave 0 (index load one tile
+//    earlier than the block-table load), so no dependent global round trip
+//    sits on the critical path of a tile.
 //  * QK: S^T[token, head] = C . Q^T with v_mfma_f32_16x16x32_bf16 (M = 16
 //    tokens, N = 16 heads, K = 32 dims, 18 steps over 576 dims); Q stays in
-//    registers for the whole workgroup.
-//  * Softmax: the S^T accumulator layout gives each lane one head and 4
-//    tokens of each token tile, so the running max / sum need only two
-//    cross-lane steps per tile, and the probabilities are already in the B
-//    operand layout of the PV product.
+//    registers.  The S^T accumulator gives each lane one head and 4 tokens of
+//    a token tile -- exactly the B-operand layout of PV.
 //  * PV: O^T[dim, head] += V^T . P^T (M = 16 dims, N = 16 heads, K = 32
 //    tokens) with V^T read from the token-major LDS tile.
-//  * Each wave owns 16 heads x 128 dims (16-head rows) or 16 heads x 256 dims
-//    (the rest, in 32-head workgroups), so the output accumulator stays at
-//    <= 64 VGPRs; the head blocks of one (row, split) are placed on one XCD so
-//    their identical gathers meet in that XCD's L2.
+//  * The head blocks of one (row, split) are placed on one XCD (workgroup ids
+//    8 apart) so their identical gathers meet in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,8 +48,7 @@ constexpr int kChunks = kKvDim * 2 / 16;       // 72 sixteen-byte chunks per lat
 constexpr int kRowChunks = kChunks + 1;        // 73: one pad chunk per LDS row
 constexpr int kRowStride = kRowChunks * 16;    // 1168 bytes
 constexpr int kTileBytes = kTile * kRowStride; // 74752
-constexpr int kTileLoads = kTile * kRowChunks / 64;     // 73 wave-wide 1 KB loads per tile
-constexpr int kLoadsPerWave = (kTileLoads + 3) / 4;    // 19 (the last wave issues 16)
+constexpr int kTileLoads = kTile * kRowChunks / 64;   // 73 wave-wide 1 KB loads per tile
 
 __device__ __attribute__((aligned(16))) uint4 g_zero_row[kChunks] = {};
 
@@ -59,12 +63,14 @@ struct MlaArgs {
   float scale_log2;        // softmax_scale * log2(e)
   int splits;
   int split_slots;         // k slots per split (multiple of 64)
-  int head_blocks;         // H / 16 for H == 16 (1), else H / 32
+  int head_blocks;         // workgroups per (row, split)
   uint16_t* out;
   float* lse;
   float* part_acc;         // [splits, R, H, 512]
   float* part_ml;          // [splits, R, H, 2]: running max (log2 domain), sum
 };
+
+typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   v8bf r;
@@ -72,14 +78,38 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   return r;
 }
 
-template <int DQ>
-__global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
-  constexpr int HT = 4 / DQ;          // head tiles of 16 per workgroup
-  constexpr int DW = kVDim / DQ;      // output dims per wave
-  constexpr int NDT = DW / 16;        // dim tiles per wave
-  __shared__ __attribute__((aligned(16))) unsigned char s_tile[kTileBytes];
-  __shared__ const unsigned char* s_rowptr[kTile];
-  __shared__ uint64_t s_mask;
+// 32-bit LDS address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (lds wave-uniform).  Written as inline asm so the compiler does not treat
+// the transfer as an LDS store that every later LDS read must wait for: it
+// would otherwise drain the gather of the next tile before reading the current
+// one.  The kernel waits for these loads itself (vmcnt) before its barrier.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+
+// LDS of one workgroup with HT head tiles and TP parts per head tile.
+template <int HT, int TP>
+struct MlaShared {
+  unsigned char tile[2][kTileBytes];                 // double-buffered gathered rows
+  const unsigned char* rowptr[2][kTile];             // source row of each slot
+  uint64_t mask[2];                                   // valid slots of each buffer
+  uint2 p[HT][4][4][16];                             // bf16 probabilities [tile][g][head]
+  float tmax[HT][TP][16];                             // per-part tile maxima
+};
+
+template <int HT, int TP>
+__global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
+  constexpr int NW = HT * TP;          // waves
+  constexpr int TPT = 4 / TP;          // token tiles of 16 scored per wave
+  constexpr int DW = kVDim / TP;       // output dims per wave
+  constexpr int NDT = DW / 16;         // dim tiles per wave
+  constexpr int LPW = (kTileLoads + NW - 1) / NW;   // gather loads per wave
+  __shared__ MlaShared<HT, TP> sh;
 
   const int R = a.batch.num_rows;
   const int lane = lane_id();
@@ -87,9 +117,6 @@ __global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
   const int g = lane >> 4;            // k-group of the MFMA operands
   const int n16 = lane & 15;
 
-  // Workgroup -> (row, split, head block); the head blocks of one (row, split)
-  // land on the same XCD (workgroup ids 8 apart) so their identical gathers
-  // meet in that XCD's L2.
   const int bid = blockIdx.x;
   const int q8 = bid >> 3;
   const int hb = q8 % a.head_blocks;
@@ -98,14 +125,54 @@ __global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
   const int r = rest / a.splits;
   const int sp = rest % a.splits;
 
-  const int ht = wave % HT, dq = wave / HT;
+  const int ht = wave % HT, part = wave / HT;
   const int h = hb * (16 * HT) + ht * 16 + n16;
-  const int d_base = dq * DW;
+  const int d_base = part * DW;
 
   const int b = seq_of_row(a.batch.query_start, a.batch.num_seqs, r);
   const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
   const int slot0 = sp * a.split_slots;
   const int slot1 = min(slot0 + a.split_slots, a.k);
+  const int ntiles = (slot1 - slot0 + kTile - 1) / kTile;
+
+  // Row pointer of slot j (wave 0 only): index -> block table -> page row.
+  const int32_t* idx_row = a.indices + (int64_t)r * a.k;
+  auto load_idx = [&](int t) -> int {
+    const int j = slot0 + t * kTile + lane;
+    return (t < ntiles && j < slot1) ? idx_row[j] : -1;
+  };
+  // Block-table entry of an index (not range-checked yet, so the load is not
+  // waited for until publish()).
+  auto load_page = [&](int idx) -> int {
+    return (idx >= 0 && idx < e) ? a.batch.block_table[(int64_t)b * a.batch.bt_stride + (idx >> 6)] : -1;
+  };
+  auto publish = [&](int t, int idx, int page) {
+    const bool valid = page >= 0 && page < a.batch.num_pages;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(g_zero_row);
+    if (valid) src = reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page * a.kv_stride + (idx & 63) * kKvDim);
+    sh.rowptr[t & 1][lane] = src;
+    const uint64_t m = __ballot(valid);
+    if (lane == 0) sh.mask[t & 1] = t < ntiles ? m : 0ull;
+  };
+  // Gather of tile t into buffer t & 1: LDS chunk p = 64 * load + lane holds
+  // (row p / 73, chunk p % 73); chunk 72 of a row is padding (re-reads chunk 0).
+  auto gather = [&](int t) {
+    unsigned char* dst = sh.tile[t & 1];
+    int p = (wave * LPW) * 64 + lane;
+    asm volatile("" : "+v"(p));   // recompute per tile rather than keep LPW cursors live
+    int row = p / kRowChunks;
+    int c = p - row * kRowChunks;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int blk = wave * LPW + i;
+      if (blk < kTileLoads) {
+        const unsigned char* src = sh.rowptr[t & 1][row] + (c < kChunks ? (c << 4) : 0);
+        lds_dma16(src, lds_addr(dst + blk * 1024));
+      }
+      c += 64;
+      if (c >= kRowChunks) { c -= kRowChunks; ++row; }
+    }
+  };
 
   // Q^T operand: lane supplies head h, dims 32*ks + 8*g .. +8.
   uint4 qreg[18];
@@ -114,10 +181,18 @@ __global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
   }
-  // LDS operand bases: QK reads token n16 (+16*tt), dims 8*g (+32*ks);
-  // PV reads tokens 4*g (+16*tt + i), dim d_base + n16 (+16*dt).
-  const unsigned char* qk_base = s_tile + n16 * kRowStride + 16 * g;
-  const unsigned char* pv_base = s_tile + 4 * g * kRowStride + 2 * (d_base + n16);
+
+  // prologue: row pointers of tiles 0 and 1, indices of tile 2, gather of tile 0
+  int idx_next = -1;  // indices of tile t + 2 (wave 0)
+  if (wave == 0) {
+    const int i0 = load_idx(0), i1 = load_idx(1);
+    idx_next = load_idx(2);
+    const int p0 = load_page(i0), p1 = load_page(i1);
+    publish(0, i0, p0);
+    publish(1, i1, p1);
+  }
+  __syncthreads();
+  if (sh.mask[0] != 0ull) gather(0);
 
   v4f acc[NDT];
 #pragma unroll
@@ -125,119 +200,120 @@ __global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
   float m_run = kMaskSentinel;   // running max of the log2-domain scores of head h
   float l_part = 0.f;            // this lane's share of the running sum
 
-  for (int t0 = slot0; t0 < slot1; t0 += kTile) {
-    __syncthreads();  // the previous tile is no longer being read
-    if (threadIdx.x < kTile) {
-      const int j = t0 + (int)threadIdx.x;
-      const int idx = j < slot1 ? a.indices[(int64_t)r * a.k + j] : -1;
-      bool valid = idx >= 0 && idx < e;
-      const unsigned char* src = reinterpret_cast<const unsigned char*>(g_zero_row);
-      if (valid) {
-        const int page = a.batch.block_table[(int64_t)b * a.batch.bt_stride + (idx >> 6)];
-        valid = page >= 0 && page < a.batch.num_pages;
-        if (valid) src = reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page * a.kv_stride + (idx & 63) * kKvDim);
-      }
-      s_rowptr[threadIdx.x] = src;
-      const uint64_t m = __ballot(valid);
-      if (threadIdx.x == 0) s_mask = m;
-    }
-    __syncthreads();
-    const uint64_t mask = s_mask;
-    if (mask == 0) continue;
-
-    // Gather: LDS chunk p = 64 * load + lane holds (row p / 73, chunk p % 73);
-    // chunk 72 of each row is padding and re-reads chunk 0 of the row.
-    {
-      int p = (wave * kLoadsPerWave) * 64 + lane;
-      // Recompute the cursor per tile instead of keeping 19 hoisted copies of it
-      // live across the loop (they would not fit in registers).
-      asm volatile("" : "+v"(p));
-      int t = p / kRowChunks;
-      int c = p - t * kRowChunks;
-#pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int blk = wave * kLoadsPerWave + i;
-        if (blk < kTileLoads) {
-          const unsigned char* src = s_rowptr[t] + (c < kChunks ? (c << 4) : 0);
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                           reinterpret_cast<void*>(s_tile + blk * 1024), 16, 0, 0);
-        }
-        c += 64;
-        if (c >= kRowChunks) { c -= kRowChunks; ++t; }
-      }
-    }
+  for (int t = 0; t < ntiles; ++t) {
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // S^T = C . Q^T for the 4 token tiles of 16
-    v4f s[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      s[tt] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const uint4 cv = *reinterpret_cast<const uint4*>(qk_base + tt * 16 * kRowStride + 64 * ks);
-        s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(cv), as_v8bf(qreg[ks]), s[tt], 0, 0, 0);
-      }
+    __syncthreads();                                   // tile t landed; rowptr(t+1) ready
+    const uint64_t mask = sh.mask[t & 1];
+    // Wave 0 starts the row pointers of tile t + 2: the block-table load goes
+    // out before the gather of tile t + 1, so waiting for it at publish() does
+    // not wait for the gather (vector loads retire in issue order).
+    int idx_cur = -1, page_cur = -1;
+    if (wave == 0) {
+      idx_cur = idx_next;
+      page_cur = load_page(idx_cur);
     }
-    // online softmax (log2 domain); lane holds tokens 16*tt + 4*g + i of head h
-    float tmax = kMaskSentinel;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool v = (mask >> (tt * 16 + 4 * g + i)) & 1ull;
-        const float z = v ? s[tt][i] * a.scale_log2 : kMaskSentinel;
-        s[tt][i] = z;
-        tmax = fmaxf(tmax, z);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool v = (mask >> (tt * 16 + 4 * g + i)) & 1ull;
-        const float pv = v ? exp2f(s[tt][i] - m_new) : 0.f;
-        s[tt][i] = pv;
-        psum += pv;
-      }
-    l_part = l_part * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+    if (t + 1 < ntiles && sh.mask[(t + 1) & 1] != 0ull) gather(t + 1);
+    if (wave == 0) idx_next = load_idx(t + 3);
 
-    // O^T += V^T . P^T, 32 tokens (two token tiles) per MFMA; k slot i of lane
-    // group g is token 16*(2tp) + 4g + i, slot 4 + i is token 16*(2tp+1) + 4g + i.
+    if (mask != 0ull) {
+      const unsigned char* tile = sh.tile[t & 1];
+      // scores of this wave's token tiles
+      v4f s[TPT];
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp) {
-      v8bf pb;
+      for (int u = 0; u < TPT; ++u) {
+        const int tt = part * TPT + u;
+        const unsigned char* cb = tile + (tt * 16 + n16) * kRowStride + 16 * g;
+        s[u] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (__bf16)s[2 * tp][i];
-        pb[4 + i] = (__bf16)s[2 * tp + 1][i];
+        for (int ks = 0; ks < 18; ++ks) {
+          const uint4 cv = *reinterpret_cast<const uint4*>(cb + 64 * ks);
+          s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(cv), as_v8bf(qreg[ks]), s[u], 0, 0, 0);
+        }
       }
+      float tmax = kMaskSentinel;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const unsigned char* vb = pv_base + (2 * tp) * 16 * kRowStride + 32 * dt;
-        v8s vv;
+      for (int u = 0; u < TPT; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          vv[i] = *reinterpret_cast<const short*>(vb + i * kRowStride);
-          vv[4 + i] = *reinterpret_cast<const short*>(vb + (16 + i) * kRowStride);
+          const int tok = (part * TPT + u) * 16 + 4 * g + i;
+          const bool v = (mask >> tok) & 1ull;
+          const float z = v ? s[u][i] * a.scale_log2 : kMaskSentinel;
+          s[u][i] = z;
+          tmax = fmaxf(tmax, z);
         }
-        v8bf va;
-        __builtin_memcpy(&va, &vv, 16);
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      if (TP > 1) {
+        if (g == 0) sh.tmax[ht][part][n16] = tmax;
+        __syncthreads();
+#pragma unroll
+        for (int pp = 0; pp < TP; ++pp) tmax = fmaxf(tmax, sh.tmax[ht][pp][n16]);
+      }
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        uint2 pk;
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = (part * TPT + u) * 16 + 4 * g + i;
+          const bool v = (mask >> tok) & 1ull;
+          pv[i] = v ? exp2f(s[u][i] - m_new) : 0.f;
+          psum += pv[i];
+        }
+        v4bf16 b4;
+        b4[0] = (__bf16)pv[0]; b4[1] = (__bf16)pv[1]; b4[2] = (__bf16)pv[2]; b4[3] = (__bf16)pv[3];
+        __builtin_memcpy(&pk, &b4, 8);
+        sh.p[ht][part * TPT + u][g][n16] = pk;
+      }
+      l_part = l_part * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      __syncthreads();                                 // probabilities of all token tiles
+
+      // O^T += V^T . P^T over the 64 tokens, 32 per MFMA: k slot i of lane group
+      // g is token 32tp + 4g + i, slot 4 + i is token 32tp + 16 + 4g + i.
+      const unsigned char* pv_base = tile + 4 * g * kRowStride + 2 * (d_base + n16);
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        const uint2 pa = sh.p[ht][2 * tp][g][n16];
+        const uint2 pb2 = sh.p[ht][2 * tp + 1][g][n16];
+        uint4 pcat = make_uint4(pa.x, pa.y, pb2.x, pb2.y);
+        const v8bf pb = as_v8bf(pcat);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const unsigned char* vb = pv_base + (2 * tp) * 16 * kRowStride + 32 * dt;
+          v8s vv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vv[i] = *reinterpret_cast<const short*>(vb + i * kRowStride);
+            vv[4 + i] = *reinterpret_cast<const short*>(vb + (16 + i) * kRowStride);
+          }
+          v8bf va;
+          __builtin_memcpy(&va, &vv, 16);
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+        }
       }
     }
+    // the tile's masks and row pointers of buffer t & 1 are no longer read:
+    // wave 0 publishes tile t + 2 there
+    if (wave == 0) publish(t + 2, idx_cur, page_cur);
   }
 
+  // l of head h over all tokens: lane groups, then the parts of the head tile
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
+  if (TP > 1) {
+    __syncthreads();
+    if (g == 0) sh.tmax[ht][part][n16] = l_tot;
+    __syncthreads();
+    l_tot = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < TP; ++pp) l_tot += sh.tmax[ht][pp][n16];
+  }
 
   if (a.splits == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -249,7 +325,7 @@ __global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
       pk.y = (uint32_t)f32_to_bf16_rne(acc[dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[dt][3] * inv) << 16);
       *reinterpret_cast<uint2*>(op + dt * 16) = pk;
     }
-    if (dq == 0 && g == 0)
+    if (part == 0 && g == 0)
       a.lse[(int64_t)r * a.H + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
     const int64_t base = ((int64_t)sp * R + r) * a.H + h;
@@ -257,7 +333,7 @@ __global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<float4*>(pa + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (dq == 0 && g == 0) {
+    if (part == 0 && g == 0) {
       a.part_ml[base * 2] = l_tot > 0.f ? m_run : kMaskSentinel;
       a.part_ml[base * 2 + 1] = l_tot;
     }
@@ -265,25 +341,42 @@ __global__ void __launch_bounds__(256, 2) sparse_mla_kernel(MlaArgs a) {
 }
 
 // N-way merge of the split partials: one wave per (row, head), 8 dims per lane.
+// The split maxima and sums are read lane-parallel (lane i <-> split i), and
+// the accumulator loads of all splits are issued before they are combined.
 __global__ void __launch_bounds__(256) sparse_mla_merge_kernel(MlaArgs a) {
   const int R = a.batch.num_rows;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)R * a.H) return;
   const int lane = lane_id();
   const int64_t RH = (int64_t)R * a.H;
-  float M = kMaskSentinel;
-  for (int i = 0; i < a.splits; ++i) M = fmaxf(M, a.part_ml[(i * RH + pair) * 2]);
-  float L = 0.f;
+  float mi = kMaskSentinel, li = 0.f;
+  if (lane < a.splits) {
+    mi = a.part_ml[(lane * RH + pair) * 2];
+    li = a.part_ml[(lane * RH + pair) * 2 + 1];
+  }
+  const float M = wave_max(mi);
+  const float wi = li > 0.f ? exp2f(mi - M) : 0.f;
+  const float L = wave_sum(li * wi);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < a.splits; ++i) {
-    const float mi = a.part_ml[(i * RH + pair) * 2];
-    const float li = a.part_ml[(i * RH + pair) * 2 + 1];
-    const float wgt = li > 0.f ? exp2f(mi - M) : 0.f;
-    L += li * wgt;
-    const float4* src = reinterpret_cast<const float4*>(a.part_acc + (i * RH + pair) * kVDim + 8 * lane);
-    const float4 x0 = src[0], x1 = src[1];
-    o[0] += wgt * x0.x; o[1] += wgt * x0.y; o[2] += wgt * x0.z; o[3] += wgt * x0.w;
-    o[4] += wgt * x1.x; o[5] += wgt * x1.y; o[6] += wgt * x1.z; o[7] += wgt * x1.w;
+  constexpr int U = 8;
+  for (int i0 = 0; i0 < a.splits; i0 += U) {
+    float4 x[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < a.splits) {
+        const float4* src = reinterpret_cast<const float4*>(a.part_acc + ((i0 + u) * RH + pair) * kVDim + 8 * lane);
+        x[u][0] = src[0];
+        x[u][1] = src[1];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u < a.splits) {
+        const float wgt = __shfl(wi, i0 + u, 64);
+        o[0] += wgt * x[u][0].x; o[1] += wgt * x[u][0].y; o[2] += wgt * x[u][0].z; o[3] += wgt * x[u][0].w;
+        o[4] += wgt * x[u][1].x; o[5] += wgt * x[u][1].y; o[6] += wgt * x[u][1].z; o[7] += wgt * x[u][1].w;
+      }
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint4 pk;
@@ -299,13 +392,14 @@ __global__ void __launch_bounds__(256) sparse_mla_merge_kernel(MlaArgs a) {
 
 MlaPlan plan_sparse_mla(int num_rows, int max_seq_len, int H, int k, int num_splits, int num_cus) {
   MlaPlan p{};
-  const int head_blocks = H == 16 ? 1 : H / 32;   // 16- or 32-head workgroups
+  const int head_blocks = H <= 32 ? 1 : H / 64;   // 16-, 32- or 64-head workgroups
   const int live = max(1, min(k, max(max_seq_len, 1)));
   const int tiles = (live + kTile - 1) / kTile;      // tiles that can hold valid entries
   const int all_tiles = (k + kTile - 1) / kTile;
   int s = num_splits;
   if (s <= 0) {
-    // about one 4-wave workgroup per CU, never more splits than useful tiles
+    // one workgroup per CU (a workgroup holds two 73 KB tiles of LDS), never
+    // more splits than tiles that can hold valid entries
     const int64_t groups = (int64_t)max(num_rows, 1) * head_blocks;
     s = (int)((num_cus + groups - 1) / groups);
     s = max(1, min(s, tiles));
@@ -354,9 +448,11 @@ hipError_t launch_sparse_mla(const BatchArgs& batch, const uint16_t* q, int H, c
   const int64_t units = (int64_t)batch.num_rows * p.splits;
   const int64_t grid = (units + 7) / 8 * 8 * p.head_blocks;
   if (H == 16) {
-    hipLaunchKernelGGL(sparse_mla_kernel<4>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+  } else if (H == 32) {
+    hipLaunchKernelGGL((sparse_mla_kernel<2, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL(sparse_mla_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<4, 2>), dim3((unsigned)grid), dim3(512), 0, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
