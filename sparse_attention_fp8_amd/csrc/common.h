@@ -46,6 +46,27 @@ __device__ __forceinline__ int seq_of_row(const int* qs, int num_seqs, int r) {
   return lo;
 }
 
+// Wave-cooperative seq_of_row: every lane of a full wave calls it with the same
+// r.  Two rounds of lane-parallel loads (a 64-way fan-out over query_start,
+// then 64 entries within the chosen stride) replace the binary search's chain
+// of dependent loads; num_seqs <= 4096 keeps the stride <= 64.
+__device__ __forceinline__ int seq_of_row_wave(const int* qs, int num_seqs, int r) {
+  if (num_seqs <= 0) return -1;
+  const int lane = threadIdx.x & 63;
+  const int step = (num_seqs + 63) >> 6;
+  const int j1 = lane * step;
+  const int v1 = j1 < num_seqs ? qs[j1] : 0x7FFFFFFF;
+  const int last = qs[num_seqs];
+  const int n1 = __popcll(__ballot(v1 <= r));
+  if (n1 == 0 || r >= last) return -1;
+  if (step == 1) return n1 - 1;
+  const int lo = (n1 - 1) * step;
+  const int j2 = lo + lane;
+  const int v2 = (lane < step && j2 < num_seqs) ? qs[j2] : 0x7FFFFFFF;
+  const int n2 = __popcll(__ballot(v2 <= r));
+  return lo + n2 - 1;
+}
+
 // Causal extent of row r of sequence b: e_r = L_b - q_len_b + i + 1, in [0, L_b].
 __device__ __forceinline__ int row_extent(const BatchArgs& a, int b, int r) {
   const int q0 = a.query_start[b], q1 = a.query_start[b + 1];

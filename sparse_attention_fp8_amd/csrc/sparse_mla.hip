@@ -45,10 +45,9 @@ namespace {
 
 constexpr int kTile = 64;                      // selected tokens per LDS tile
 constexpr int kChunks = kKvDim * 2 / 16;       // 72 sixteen-byte chunks per latent row
-constexpr int kRowChunks = kChunks + 1;        // 73: one pad chunk per LDS row
-constexpr int kRowStride = kRowChunks * 16;    // 1168 bytes
-constexpr int kTileBytes = kTile * kRowStride; // 74752
-constexpr int kTileLoads = kTile * kRowChunks / 64;   // 73 wave-wide 1 KB loads per tile
+constexpr int kChunkGroups = kChunks / 8;      // 9 groups of 128 B per row
+constexpr int kRowGroups = kTile / 8;          // 8 groups of 8 rows per tile
+constexpr int kTileBytes = kTile * kChunks * 16;   // 73728
 
 __device__ __attribute__((aligned(16))) uint4 g_zero_row[kChunks] = {};
 
@@ -71,6 +70,14 @@ struct MlaArgs {
 };
 
 typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane n receives element
+// n % 4 of the 8-byte vectors addressed by lanes n / 4 + 4 j, j = 0..3.
+__device__ __forceinline__ v4s lds_read_tr16(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(const __attribute__((address_space(3))) void*)p);
+}
 
 __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   v8bf r;
@@ -108,7 +115,9 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   constexpr int TPT = 4 / TP;          // token tiles of 16 scored per wave
   constexpr int DW = kVDim / TP;       // output dims per wave
   constexpr int NDT = DW / 16;         // dim tiles per wave
-  constexpr int LPW = (kTileLoads + NW - 1) / NW;   // gather loads per wave
+  constexpr int RGW = kRowGroups / NW; // row groups each wave gathers
+  static_assert(RGW * NW == kRowGroups, "waves must split the row groups evenly");
+  static_assert(DW % 128 == 0, "PV swizzle terms assume 128-dim aligned parts");
   __shared__ MlaShared<HT, TP> sh;
 
   const int R = a.batch.num_rows;
@@ -129,8 +138,6 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   const int h = hb * (16 * HT) + ht * 16 + n16;
   const int d_base = part * DW;
 
-  const int b = seq_of_row(a.batch.query_start, a.batch.num_seqs, r);
-  const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
   const int slot0 = sp * a.split_slots;
   const int slot1 = min(slot0 + a.split_slots, a.k);
   const int ntiles = (slot1 - slot0 + kTile - 1) / kTile;
@@ -141,39 +148,59 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
     const int j = slot0 + t * kTile + lane;
     return (t < ntiles && j < slot1) ? idx_row[j] : -1;
   };
-  // Block-table entry of an index (not range-checked yet, so the load is not
-  // waited for until publish()).
+  int b = -1, e = 0;
+  // The block-table load needs only idx < max_seq_len to stay inside the row;
+  // the causal extent e and the page range are checked when the pointer is
+  // published, so the wait for that load comes as late as possible.
   auto load_page = [&](int idx) -> int {
-    return (idx >= 0 && idx < e) ? a.batch.block_table[(int64_t)b * a.batch.bt_stride + (idx >> 6)] : -1;
+    return (b >= 0 && idx >= 0 && idx < a.batch.max_seq_len)
+               ? a.batch.block_table[(int64_t)b * a.batch.bt_stride + (idx >> 6)] : -1;
   };
   auto publish = [&](int t, int idx, int page) {
-    const bool valid = page >= 0 && page < a.batch.num_pages;
+    const bool valid = idx >= 0 && idx < e && page >= 0 && page < a.batch.num_pages;
     const unsigned char* src = reinterpret_cast<const unsigned char*>(g_zero_row);
     if (valid) src = reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page * a.kv_stride + (idx & 63) * kKvDim);
     sh.rowptr[t & 1][lane] = src;
     const uint64_t m = __ballot(valid);
     if (lane == 0) sh.mask[t & 1] = t < ntiles ? m : 0ull;
   };
-  // Gather of tile t into buffer t & 1: LDS chunk p = 64 * load + lane holds
-  // (row p / 73, chunk p % 73); chunk 72 of a row is padding (re-reads chunk 0).
+  // Gather of tile t into buffer t & 1.  LDS layout of a tile: 1 KB block
+  // (cg, rg) = (128-B column group of the row, group of 8 rows) at
+  // (8 cg + rg) KB; inside it row r8 takes 128 B whose 16-B slot s holds the
+  // row's chunk s ^ r8.  One wave-wide load fills one block: lane l copies
+  // slot l & 7 of row l >> 3, so each load reads eight whole 128-B lines and
+  // each lane needs one row pointer per row group.
+  constexpr int ND = RGW * kChunkGroups;   // gather loads per wave and tile
+  auto gather_src = [&](int t, int j) -> const unsigned char* {
+    return sh.rowptr[t & 1][(wave * RGW + j) * 8 + (lane >> 3)] + (((lane & 7) ^ (lane >> 3)) << 4);
+  };
+  auto gather_one = [&](const unsigned char* const* src, uint32_t dst, int i) {
+    const int j = i / kChunkGroups, cg = i % kChunkGroups;
+    lds_dma16(src[j] + cg * 128, dst + (cg * kRowGroups + wave * RGW + j) * 1024);
+  };
   auto gather = [&](int t) {
-    unsigned char* dst = sh.tile[t & 1];
-    int p = (wave * LPW) * 64 + lane;
-    asm volatile("" : "+v"(p));   // recompute per tile rather than keep LPW cursors live
-    int row = p / kRowChunks;
-    int c = p - row * kRowChunks;
+    const unsigned char* src[RGW];
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int blk = wave * LPW + i;
-      if (blk < kTileLoads) {
-        const unsigned char* src = sh.rowptr[t & 1][row] + (c < kChunks ? (c << 4) : 0);
-        lds_dma16(src, lds_addr(dst + blk * 1024));
-      }
-      c += 64;
-      if (c >= kRowChunks) { c -= kRowChunks; ++row; }
-    }
+    for (int j = 0; j < RGW; ++j) src[j] = gather_src(t, j);
+    const uint32_t dst = lds_addr(sh.tile[t & 1]);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) gather_one(src, dst, i);
   };
 
+  // Prologue.  Vector loads retire in issue order, so wave 0's chain (indices
+  // with the sequence search, then the block table) goes out before any Q
+  // load: waiting for a link of the chain never waits for Q.
+  int idx_next = -1;   // indices of tile t + 2 (wave 0)
+  if (wave == 0) {
+    const int i0 = load_idx(0), i1 = load_idx(1);
+    idx_next = load_idx(2);
+    b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
+    e = b >= 0 ? row_extent(a.batch, b, r) : 0;
+    const int p0 = load_page(i0), p1 = load_page(i1);
+    publish(0, i0, p0);
+    publish(1, i1, p1);
+  }
+  asm volatile("" ::: "memory");
   // Q^T operand: lane supplies head h, dims 32*ks + 8*g .. +8.
   uint4 qreg[18];
   {
@@ -181,18 +208,22 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
   }
-
-  // prologue: row pointers of tiles 0 and 1, indices of tile 2, gather of tile 0
-  int idx_next = -1;  // indices of tile t + 2 (wave 0)
-  if (wave == 0) {
-    const int i0 = load_idx(0), i1 = load_idx(1);
-    idx_next = load_idx(2);
-    const int p0 = load_page(i0), p1 = load_page(i1);
-    publish(0, i0, p0);
-    publish(1, i1, p1);
-  }
   __syncthreads();
   if (sh.mask[0] != 0ull) gather(0);
+
+  // Operand addresses (bytes into a tile).  QK: lane reads row tt*16 + n16,
+  // chunk 4 ks + g; the swizzle term is x0 for even ks and x0 ^ 64 for odd.
+  const int r8 = n16 & 7;
+  const int qk0 = (n16 >> 3) * 1024 + r8 * 128 + (((g ^ r8) << 4));
+  const int qk1 = (n16 >> 3) * 1024 + r8 * 128 + (((g ^ r8) << 4) ^ 64);
+  // PV: the V^T operand comes from two transposed reads per MFMA.  Lane n16
+  // of group g addresses token 32 tp + 4 g + n16 / 4 (+16 for the second
+  // read), dims d_base + 16 dt + 4 (n16 % 4) .. +3, so after the transpose it
+  // holds dim d_base + 16 dt + n16 of tokens 32 tp + 4 g + j.  The swizzle
+  // slot is Lt ^ 2 (dt & 3) with the lane part Lt.
+  const int pv_Lt = ((n16 >> 1) & 1) ^ (((g & 1) << 2) | (n16 >> 2));
+  const int pv_lane = (g >> 1) * 1024 + (((g & 1) << 2) + (n16 >> 2)) * 128 + 8 * (n16 & 1);
+  const int pv_part = (d_base >> 6) * (kRowGroups * 1024);
 
   v4f acc[NDT];
 #pragma unroll
@@ -212,8 +243,21 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
       idx_cur = idx_next;
       page_cur = load_page(idx_cur);
     }
-    if (t + 1 < ntiles && sh.mask[(t + 1) & 1] != 0ull) gather(t + 1);
     if (wave == 0) idx_next = load_idx(t + 3);
+    // The gather of tile t + 1 is spread over this tile's QK steps: issued in
+    // one burst, its loads would stall the wave on the memory pipeline's
+    // backpressure before any compute of tile t starts.
+    const bool pre = t + 1 < ntiles && sh.mask[(t + 1) & 1] != 0ull;
+    const unsigned char* gsrc[RGW];
+    const uint32_t gdst = lds_addr(sh.tile[(t + 1) & 1]);
+    if (pre) {
+#pragma unroll
+      for (int j = 0; j < RGW; ++j) gsrc[j] = gather_src(t + 1, j);
+    }
+    if (pre && mask == 0ull) {
+#pragma unroll
+      for (int i = 0; i < ND; ++i) gather_one(gsrc, gdst, i);
+    }
 
     if (mask != 0ull) {
       const unsigned char* tile = sh.tile[t & 1];
@@ -222,11 +266,16 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
         const int tt = part * TPT + u;
-        const unsigned char* cb = tile + (tt * 16 + n16) * kRowStride + 16 * g;
         s[u] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 18; ++ks) {
-          const uint4 cv = *reinterpret_cast<const uint4*>(cb + 64 * ks);
+          constexpr int NQ = TPT * 18;
+          const int q = u * 18 + ks;
+#pragma unroll
+          for (int i = 0; i < ND; ++i)
+            if (i * NQ / ND == q && pre) gather_one(gsrc, gdst, i);
+          const unsigned char* cb = tile + ((ks & 1) ? qk1 : qk0) + (ks >> 1) * (kRowGroups * 1024) + tt * 2048;
+          const uint4 cv = *reinterpret_cast<const uint4*>(cb);
           s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(cv), as_v8bf(qreg[ks]), s[u], 0, 0, 0);
         }
       }
@@ -276,7 +325,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 
       // O^T += V^T . P^T over the 64 tokens, 32 per MFMA: k slot i of lane group
       // g is token 32tp + 4g + i, slot 4 + i is token 32tp + 16 + 4g + i.
-      const unsigned char* pv_base = tile + 4 * g * kRowStride + 2 * (d_base + n16);
+      const unsigned char* pv_base = tile + pv_part + pv_lane;
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
         const uint2 pa = sh.p[ht][2 * tp][g][n16];
@@ -285,13 +334,11 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
         const v8bf pb = as_v8bf(pcat);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const unsigned char* vb = pv_base + (2 * tp) * 16 * kRowStride + 32 * dt;
-          v8s vv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vv[i] = *reinterpret_cast<const short*>(vb + i * kRowStride);
-            vv[4 + i] = *reinterpret_cast<const short*>(vb + (16 + i) * kRowStride);
-          }
+          const unsigned char* vb = pv_base + (dt >> 2) * (kRowGroups * 1024) + tp * 4096 +
+                                    ((pv_Lt ^ (2 * (dt & 3))) << 4);
+          const v4s lo = lds_read_tr16(vb);
+          const v4s hi = lds_read_tr16(vb + 2048);
+          const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           v8bf va;
           __builtin_memcpy(&va, &vv, 16);
           acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);

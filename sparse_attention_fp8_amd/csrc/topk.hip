@@ -260,7 +260,7 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
   __shared__ Shared sh;
   const int r = blockIdx.x / a.nchunks;
   const int c = blockIdx.x % a.nchunks;
-  const int b = seq_of_row(a.batch.query_start, a.batch.num_seqs, r);
+  const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
   const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
   const int k = a.k;
   const float* row = a.logits + (int64_t)r * a.logits_stride;
@@ -313,7 +313,7 @@ template <int KPT>
 __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
   __shared__ Shared sh;
   const int r = blockIdx.x;
-  const int b = seq_of_row(a.batch.query_start, a.batch.num_seqs, r);
+  const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
   const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
   if (e <= kChunk) return;
   const int k = a.k;
