@@ -9,22 +9,31 @@
 // registers.
 //  * One 1024-thread workgroup takes up to kChunk = 32768 keys of a row;
 //    thread t holds the KPT consecutive keys [t*KPT, (t+1)*KPT) in VGPRs
-//    (KPT = 8, 16 or 32, picked on the host from the longest row), so the
-//    keys are read from memory once and index order is thread order.
-//  * Up to three digit passes (11, 11 and 10 bits) build an LDS histogram of
-//    the keys that still match the threshold prefix; one wave scans the 2048
-//    bins from the top.  A pass stops the search early when the threshold
-//    bin is taken whole.  Only a few percent of the keys survive pass one.
-//  * Emission: each thread counts its keys above the threshold and equal to
-//    it, one block-wide scan gives every thread its output offset and tie
-//    budget, and each thread writes its selected indices in order -- ties at
-//    the threshold are taken lowest index first, so the output is sorted and
-//    deterministic without any sort.
+//    (KPT = 8, 16 or 32, picked on the host from the longest row), so index
+//    order is thread order.  The keys reach the registers through LDS: each
+//    wave copies its 64*KPT floats with line-coalesced global->LDS loads into
+//    an XOR-swizzled layout and reads its own keys back without bank
+//    conflicts (a direct per-thread float4 read would touch 64 cache lines
+//    per wave instruction).
+//  * Up to three digit passes (11, 11 and 10 bits).  Pass one counts every
+//    key into 8 interleaved copies of a 2048-bin LDS histogram (lane l adds
+//    to copy l % 8), which spreads the atomics of the few hot bins; a block
+//    scan over the bins from the top finds the threshold bin.  A pass stops
+//    the search when the threshold bin is taken whole.  The keys of the
+//    threshold bin (usually a few percent) are compacted into an LDS list and
+//    passes two and three run over that list.
+//  * Emission: each thread forms bit masks of its keys above the threshold
+//    and equal to it; one block scan gives every thread its output offset and
+//    tie budget; each thread walks the set bits of its mask, so it writes
+//    only selected indices, in order -- ties at the threshold are taken
+//    lowest index first and the output is sorted without any sort.
 //  * A longer row is cut into chunks whose winners are kept as (key, index)
 //    candidates.  Every member of the row's top-k is in its own chunk's top-k
 //    (fewer than k entries precede it in the row, hence in the chunk), so one
 //    more selection over the concatenated candidates -- already in index
 //    order -- is exact (the chunked exact top-k argument of the pages).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,6 +46,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 32768;          // keys per workgroup in the row pass
 constexpr int kMergeMax = 65536;       // candidates per row in the merge pass
 constexpr int kBins = 2048;
+constexpr int kCopies = 8;             // interleaved copies of the pass-one histogram
+constexpr int kCand = 4096;            // LDS list for the threshold bin's keys
 
 struct TopkArgs {
   BatchArgs batch;
@@ -50,47 +61,127 @@ struct TopkArgs {
   int32_t* cand_count;    // [R, nchunks]
 };
 
-// LDS of one workgroup.  hist has two alternating digit histograms (so one is
-// cleared while the other is counted) plus one private overflow counter per
-// lane: keys that do not match the current prefix are counted there, which
-// keeps every atomic unconditional (no per-key branch) and conflict-free.
-constexpr int kHist = kBins + 64;
-constexpr int kCand = 4096;            // LDS list for the threshold bin's keys
+// Selection state of one workgroup.  hist1 is pass one's histogram, bin-major
+// with the copies innermost; its first kBins entries are reused by pass three
+// while hist2 serves pass two, so no pass clears a histogram it must wait for.
 struct Shared {
-  int hist[2][kHist];
-  uint32_t cand[kCand + 64];           // (+ one dummy slot per lane)
-  int out[DSA_MAX_TOPK + 64];  // staged output (+ one dummy slot per lane)
-  uint64_t wave_pair[kWaves];
+  int hist1[kBins * kCopies];
+  int hist2[kBins];
+  uint32_t cand[kCand];
+  int out[DSA_MAX_TOPK];
   int wave_tot[kWaves];
   int misc[4];
 };
 
-// Keys [t*KPT, (t+1)*KPT) of thread t.  Positions >= n get key 0: every finite
-// float and +-inf maps to a key >= 2^21, so with n > k valid keys the k-th
-// largest key is never 0 and a key-0 slot is never selected.
+// The key staging area overlaps the selection state: it is dead once every
+// wave has read its keys back (a barrier separates the two uses).
+template <int KPT>
+union TopkLds {
+  Shared s;
+  float4 stage[kThreads * KPT / 4];
+};
+
 template <int KPT>
 struct Keys {
   uint32_t v[KPT];
 };
 
-// The float4 holding an in-range key is inside the row: logits_stride and
-// chunk starts are multiples of 4.
 template <int KPT>
-__device__ void load_float_keys(Keys<KPT>& keys, const float* src, int n) {
+using MaskT = typename std::conditional<(KPT > 32), uint64_t, uint32_t>::type;
+
+__device__ __forceinline__ int popc(uint32_t m) { return __popc(m); }
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+__device__ __forceinline__ int ctz(uint32_t m) { return __builtin_ctz(m); }
+__device__ __forceinline__ int ctz(uint64_t m) { return __builtin_ctzll(m); }
+__device__ __forceinline__ uint32_t drop_highest(uint32_t m) { return m & ~(0x80000000u >> __builtin_clz(m)); }
+__device__ __forceinline__ uint64_t drop_highest(uint64_t m) {
+  return m & ~(0x8000000000000000ull >> __builtin_clzll(m));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds
+// wave-uniform).  Inline asm: the compiler would otherwise treat the copy as an
+// LDS store that all later LDS reads wait for; the caller waits (vmcnt) itself.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Inclusive prefix sum over the 64 lanes: DPP shifts inside each row of 16
+// lanes, then the row totals are read out as scalars and added.
+__device__ __forceinline__ int wave_scan_dpp(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// Block-wide inclusive scan of one int per thread (one barrier).  Two calls
+// need a barrier between them: the second overwrites sh.wave_tot.
+__device__ __forceinline__ int block_scan(int v, Shared& sh) {
+  const int w = threadIdx.x >> 6;
+  const int incl = wave_scan_dpp(v);
+  if (lane_id() == 63) sh.wave_tot[w] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) before += (i < w) ? sh.wave_tot[i] : 0;
+  return incl + before;
+}
+
+// Keys [t*KPT, (t+1)*KPT) of thread t from src[0, n).  Positions >= n get key
+// 0: every finite float and +-inf maps to a key >= 2^21, so with n > k valid
+// keys the k-th largest key is never 0 and a key-0 slot is never selected.
+// Wave w copies the V = KPT / 4 float4s of each of its lanes to LDS: owner
+// lane L's float4 j goes to slot L V + (j ^ swz(L)) of the wave's area, with
+// swz(L) = (L / (8 / V)) % V.  Eight consecutive lanes then read eight
+// distinct 16-byte bank groups, and each group of 8 lanes of one copy
+// instruction reads one whole 128-byte line.  Float4s at or past n are not
+// read (their slot gets a copy of the row's first float4 and is masked
+// afterwards); src is 16-byte aligned and every float4 that starts below n
+// lies inside the row.
+template <int KPT>
+__device__ void load_keys(Keys<KPT>& keys, const float* src, int n, float4* stage) {
+  constexpr int V = KPT / 4;
+  constexpr int F = 8 / V;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const float4* src4 = reinterpret_cast<const float4*>(src);
+  float4* wst = stage + w * 64 * V;
+  const int f0 = w * 64 * V;                       // first float4 of this wave
+  if (4 * f0 < n) {
+    const uint32_t wdst = lds_addr(wst);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int S = 64 * i + l;                    // slot this lane fills
+      const int L = S / V;                         // owner lane of the slot
+      const int j = (S % V) ^ ((L / F) % V);       // owner's float4 index
+      const int f = f0 + L * V + j;
+      lds_dma16(4 * f < n ? src4 + f : src4, wdst + i * 1024);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
   const int base = (int)threadIdx.x * KPT;
 #pragma unroll
-  for (int j = 0; j < KPT / 4; ++j) {
+  for (int j = 0; j < V; ++j) {
     const int p = base + 4 * j;
-    if (p < n) {
-      const float4 x = *reinterpret_cast<const float4*>(src + p);
-      keys.v[4 * j] = float_key(x.x);
-      keys.v[4 * j + 1] = p + 1 < n ? float_key(x.y) : 0u;
-      keys.v[4 * j + 2] = p + 2 < n ? float_key(x.z) : 0u;
-      keys.v[4 * j + 3] = p + 3 < n ? float_key(x.w) : 0u;
-    } else {
-      keys.v[4 * j] = keys.v[4 * j + 1] = keys.v[4 * j + 2] = keys.v[4 * j + 3] = 0u;
-    }
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < n) x = wst[l * V + (j ^ ((l / F) % V))];
+    keys.v[4 * j] = p < n ? float_key(x.x) : 0u;
+    keys.v[4 * j + 1] = p + 1 < n ? float_key(x.y) : 0u;
+    keys.v[4 * j + 2] = p + 2 < n ? float_key(x.z) : 0u;
+    keys.v[4 * j + 3] = p + 3 < n ? float_key(x.w) : 0u;
   }
+  // materialise the keys here: otherwise the compiler sinks the range selects
+  // into later loops and keeps one lane mask per key alive in scalar registers
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(keys.v[j]));
 }
 
 // Candidate keys (4-byte aligned only: a row's candidates start at r * k).
@@ -99,6 +190,8 @@ __device__ void load_raw_keys(Keys<KPT>& keys, const uint32_t* src, int n) {
   const int base = (int)threadIdx.x * KPT;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) keys.v[j] = base + j < n ? src[base + j] : 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(keys.v[j]));
 }
 
 struct Selection {
@@ -106,19 +199,20 @@ struct Selection {
   int need_eq;         // how many keys equal to it are taken, lowest index first
 };
 
-// Finds the threshold digit of one pass from sh.hist-like counts `hist`
-// (bins in ascending digit order): the digit d whose bin holds the rem-th
-// largest matching key, the count of matching keys above its bin, and its bin
-// count.  One block scan over the 2048 bins (2 per thread, descending).
+// Finds the threshold digit of one pass from a histogram (bins in ascending
+// digit order, NC interleaved copies per bin): the digit d whose bin holds
+// the rem-th largest counted key, the count of keys above its bin, and its
+// bin count -> sh.misc[0..2].  Thread t takes bins 2047 - 2t and 2046 - 2t.
+template <int NC>
 __device__ __forceinline__ void find_digit(const int* hist, int rem, Shared& sh) {
-  const int w = threadIdx.x >> 6, l = lane_id();
   const int d0 = kBins - 1 - 2 * (int)threadIdx.x, d1 = d0 - 1;
-  const int c0 = hist[d0], c1 = hist[d1];
-  int incl = wave_inclusive_scan(c0 + c1);
-  if (l == 63) sh.wave_tot[w] = incl;
-  __syncthreads();
+  int c0 = 0, c1 = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) incl += (i < w) ? sh.wave_tot[i] : 0;
+  for (int c = 0; c < NC; ++c) {
+    c0 += hist[d0 * NC + c];
+    c1 += hist[d1 * NC + c];
+  }
+  const int incl = block_scan(c0 + c1, sh);
   const int excl = incl - c0 - c1;
   if (excl < rem && rem <= incl) {
     const bool first = excl + c0 >= rem;
@@ -130,60 +224,69 @@ __device__ __forceinline__ void find_digit(const int* hist, int rem, Shared& sh)
 }
 
 // Exact selection of the k largest of the n valid keys (n > k >= 1).
-//  pass 1: 11-bit top digit of every key (no prefix test needed);
-//  then the keys of the threshold bin (usually a few percent) are compacted
-//  into an LDS list and passes 2 and 3 (11 and 10 bits) run over that list;
-//  if the bin is too large for the list, passes 2 and 3 scan the registers.
+// Key 0 (an out-of-range slot) is counted nowhere, and every prefix and
+// threshold below is at least 2^21 - 1 (the threshold bin holds a valid key),
+// so the later comparisons exclude key 0 by themselves.
+//  pass 1: 11-bit top digit of every key;
+//  then the keys of the threshold bin are compacted into an LDS list and
+//  passes 2 and 3 (11 and 10 bits) run over that list; if the bin is too
+//  large for the list, passes 2 and 3 scan the registers.
 template <int KPT>
 __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   const int l = lane_id();
-  for (int i = threadIdx.x; i < kHist; i += kThreads) { sh.hist[0][i] = 0; sh.hist[1][i] = 0; }
+  for (int i = threadIdx.x; i < kBins * kCopies / 4; i += kThreads)
+    reinterpret_cast<int4*>(sh.hist1)[i] = make_int4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist2[i] = 0;
   if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; sh.misc[3] = 0; }
   __syncthreads();
+  const int copy = l & (kCopies - 1);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint32_t key = keys.v[j];
-    atomicAdd(&sh.hist[0][key != 0u ? (int)(key >> 21) : kBins + l], 1);
+    if (key != 0u) atomicAdd(&sh.hist1[(int)(key >> 21) * kCopies + copy], 1);
   }
   __syncthreads();
-  find_digit(sh.hist[0], k, sh);
+  find_digit<kCopies>(sh.hist1, k, sh);
   uint32_t prefix = (uint32_t)sh.misc[0] << 21;
   int rem = k - sh.misc[1];
   const int in_bin = sh.misc[2];
   if (rem == in_bin) return Selection{prefix - 1u, 0};  // the whole bin is taken
 
+  // pass three counts into hist1's first kBins entries
+  for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist1[i] = 0;
   constexpr int shifts[2] = {10, 0};
   constexpr int widths[2] = {11, 10};
   uint32_t mask = 0xFFE00000u;
+  int* const hists[2] = {sh.hist2, sh.hist1};
   if (in_bin <= kCand) {
     // compact the bin's keys: one LDS atomic per wave reserves the slots
-    int mine = 0;
+    MaskT<KPT> mb = 0;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) mine += (keys.v[j] & mask) == prefix && keys.v[j] != 0u;
-    int incl = wave_inclusive_scan(mine);
+    for (int j = 0; j < KPT; ++j)
+      mb |= (MaskT<KPT>)((keys.v[j] & mask) == prefix) << j;
+    const int mine = popc(mb);
+    const int incl = wave_scan_dpp(mine);
     int base = 0;
-    if (l == 63) base = atomicAdd(&sh.misc[3], incl);
-    base = __shfl(base, 63, 64) + incl - mine;
+    if (l == 63 && incl > 0) base = atomicAdd(&sh.misc[3], incl);
+    base = __builtin_amdgcn_readlane(base, 63) + incl - mine;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const uint32_t key = keys.v[j];
-      const bool match = (key & mask) == prefix && key != 0u;
-      sh.cand[match ? base : kCand + l] = key;
-      base += match;
+      if ((mb >> j) & 1) {
+        sh.cand[base] = keys.v[j];
+        ++base;
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-      int* hist = sh.hist[(pass + 1) & 1];
-      for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
-      __syncthreads();
+      int* hist = hists[pass];
       const uint32_t dmask = (1u << widths[pass]) - 1u;
       for (int i = threadIdx.x; i < in_bin; i += kThreads) {
         const uint32_t key = sh.cand[i];
-        atomicAdd(&hist[(key & mask) == prefix ? (int)((key >> shifts[pass]) & dmask) : kBins + l], 1);
+        if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shifts[pass]) & dmask)], 1);
       }
       __syncthreads();
-      find_digit(hist, rem, sh);
+      find_digit<1>(hist, rem, sh);
       rem -= sh.misc[1];
       prefix |= (uint32_t)sh.misc[0] << shifts[pass];
       mask |= dmask << shifts[pass];
@@ -192,20 +295,18 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
     return Selection{prefix, rem};
   }
   // large threshold bin: passes 2 and 3 over the registers
+  __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
-    int* hist = sh.hist[(pass + 1) & 1];
-    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0;
-    __syncthreads();
+    int* hist = hists[pass];
     const uint32_t dmask = (1u << widths[pass]) - 1u;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const uint32_t key = keys.v[j];
-      const bool match = key != 0u && (key & mask) == prefix;
-      atomicAdd(&hist[match ? (int)((key >> shifts[pass]) & dmask) : kBins + l], 1);
+      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shifts[pass]) & dmask)], 1);
     }
     __syncthreads();
-    find_digit(hist, rem, sh);
+    find_digit<1>(hist, rem, sh);
     rem -= sh.misc[1];
     prefix |= (uint32_t)sh.misc[0] << shifts[pass];
     mask |= dmask << shifts[pass];
@@ -214,50 +315,50 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   return Selection{prefix, rem};
 }
 
-// Stages the selected keys' chunk positions in sh.out[0, k), in chunk order:
-// one block scan of the per-thread counts, then unconditional LDS writes
-// (unselected keys write to the lane's dummy slot).  Out-of-range slots (key
-// 0) are never taken and positions are clamped to k, so whatever the logits
-// hold (NaN included) every staged position is -1 or a valid key position.
+// Stages the selected keys' chunk positions in sh.out[0, k), in chunk order.
+// Per thread: masks of keys above the threshold (gt) and equal to it (eq);
+// one block scan of the packed counts (gt in the low 12 bits -- a prefix of gt
+// counts never exceeds k <= 2048 -- and eq above) gives the thread's output
+// offset and how many ties precede it.  The thread keeps its first
+// (need_eq - ties before it) eq keys and writes the set bits of the combined
+// mask in order.  Out-of-range slots (key 0) are never taken and positions are
+// clamped to k, so whatever the logits hold (NaN included) every staged
+// position is -1 or a valid key position.
 template <int KPT>
 __device__ void stage_selected(const Keys<KPT>& keys, Selection sel, int k, Shared& sh) {
-  const int w = threadIdx.x >> 6, l = lane_id();
   for (int i = threadIdx.x; i < k; i += kThreads) sh.out[i] = -1;
-  int ng = 0, ne = 0;
+  MaskT<KPT> gtb = 0, eqb = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint32_t key = keys.v[j];
-    ng += key > sel.threshold;
-    ne += key == sel.threshold && key != 0u;
+    gtb |= (MaskT<KPT>)(key > sel.threshold) << j;
+    eqb |= (MaskT<KPT>)(key == sel.threshold) << j;
   }
-  const uint64_t packed = (uint64_t)ng | ((uint64_t)ne << 32);
-  uint64_t incl = wave_inclusive_scan_u64(packed);
-  if (l == 63) sh.wave_pair[w] = incl;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) incl += (i < w) ? sh.wave_pair[i] : 0ull;
-  const uint64_t excl = incl - packed;
-  int g = (int)(uint32_t)excl;
-  int e = (int)(excl >> 32);
+  const int ng = popc(gtb), ne = popc(eqb);
+  const int packed = ng | (ne << 12);
+  const int excl = block_scan(packed, sh) - packed;   // barrier inside: the -1 fill is done
+  const int g = excl & 0xFFF;
+  const int e = excl >> 12;
+  int take = sel.need_eq - e;                         // ties this thread may take
+  take = take < 0 ? 0 : (take > ne ? ne : take);
+  MaskT<KPT> eqsel = eqb;
+  for (int drop = ne - take; drop > 0; --drop) eqsel = drop_highest(eqsel);   // keep the lowest `take`
+  MaskT<KPT> selb = gtb | eqsel;
+  int pos = g + min(e, sel.need_eq);
   const int base = (int)threadIdx.x * KPT;
-  const int dummy = k + l;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t key = keys.v[j];
-    const bool gt = key > sel.threshold;
-    const bool eq = key == sel.threshold && key != 0u;
-    const int pos = g + min(e, sel.need_eq);
-    const bool take = (gt || (eq && e < sel.need_eq)) && pos < k;
-    sh.out[take ? pos : dummy] = base + j;
-    g += gt;
-    e += eq;
+  while (selb != 0) {
+    const int j = ctz(selb);
+    if (pos < k) sh.out[pos] = base + j;
+    ++pos;
+    selb &= selb - 1;
   }
   __syncthreads();
 }
 
 template <int KPT>
 __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
-  __shared__ Shared sh;
+  __shared__ TopkLds<KPT> lds;
+  Shared& sh = lds.s;
   const int r = blockIdx.x / a.nchunks;
   const int c = blockIdx.x % a.nchunks;
   const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
@@ -273,7 +374,8 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
       for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < e ? i : -1;
       return;
     }
-    load_float_keys(keys, row, e);
+    load_keys(keys, row, e, lds.stage);
+    __syncthreads();   // every wave has read its keys: the staging area is free
     const Selection sel = radix_select(keys, k, sh);
     stage_selected(keys, sel, k, sh);
     for (int i = threadIdx.x; i < k; i += kThreads) out[i] = sh.out[i];
@@ -290,7 +392,7 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
   const int n = min(kChunk, e - lo);
   uint32_t* ck = a.cand_keys + slot * k;
   int32_t* ci = a.cand_idx + slot * k;
-  load_float_keys(keys, row + lo, n);
+  load_keys(keys, row + lo, n, lds.stage);
   if (n <= k) {  // a short last chunk: every key is a candidate, in order
     const int base = (int)threadIdx.x * KPT;
 #pragma unroll
@@ -299,6 +401,7 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
     if (threadIdx.x == 0) a.cand_count[slot] = n;
     return;
   }
+  __syncthreads();   // staging area free
   const Selection sel = radix_select(keys, k, sh);
   stage_selected(keys, sel, k, sh);
   for (int i = threadIdx.x; i < k; i += kThreads) {
