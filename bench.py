@@ -137,38 +137,84 @@ def main():
     splits = args.splits or dsa.sparse_mla_pick_splits(batch, H, k)
     indexer = dsa.indexer_logits_prefill if prefill else dsa.indexer_logits_paged
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-
-    def step(i, events=None):
+    def run_stage(name, i):
         t = sets[i % copies]
-        if events:
-            events[0].record()
-        indexer(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=False)
-        if events:
-            events[1].record()
-        dsa.topk(batch, logits, indices, k=k, workspace=ws_topk)
-        if events:
-            events[2].record()
-        dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
-                              num_splits=args.splits, workspace=ws_mla)
-        if events:
-            events[3].record()
+        if name == "indexer":
+            indexer(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=False)
+        elif name == "topk":
+            dsa.topk(batch, logits, indices, k=k, workspace=ws_topk)
+        else:
+            dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
+                                  num_splits=args.splits, workspace=ws_mla)
 
-    for i in range(args.warmup):
+    stages = ("indexer", "topk", "sparse_mla")
+
+    def step(i):
+        for name in stages:
+            run_stage(name, i)
+
+    # eager warm-up (also loads every code object before capture)
+    for i in range(max(args.warmup, 1)):
         step(i)
     torch.cuda.synchronize()
+
+    # One HIP graph per cache copy holds one whole step; the timed region
+    # replays exactly `steps` of them, rotating through the copies.
+    step_graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(c)
+        step_graphs.append(g)
+    # Per-stage graphs: `reps` launches of one entry point, rotating copies, so
+    # the stage's average launch duration is measured on its own stream.
+    reps = 2 * copies
+    stage_graphs = {}
+    for name in stages:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                run_stage(name, i)
+        stage_graphs[name] = g
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step_graphs[i % copies].replay()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
+    start.record(stream)
     for i in range(args.steps):
-        step(i, ev[i])
-    stop.record()
+        step_graphs[i % copies].replay()
+    stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
-    stage_ms = {
-        "indexer": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
-        "topk": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
-        "sparse_mla": float(np.mean([e[2].elapsed_time(e[3]) for e in ev])),
-    }
+
+    stage_ms = {}
+    stage_rounds = max(1, args.steps // reps)
+    for name in stages:
+        stage_graphs[name].replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(stage_rounds):
+            stage_graphs[name].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stage_ms[name] = e0.elapsed_time(e1) / (stage_rounds * reps)
+
+    # device-to-device copy rate of the same run (1 GiB), for reference
+    cbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(cbuf)
+    cdst.copy_(cbuf)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        cdst.copy_(cbuf)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * cbuf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del cbuf, cdst
+
     total_bytes = nbytes["indexer"] + nbytes["topk"] + nbytes["sparse_mla"]
     if prefill:
         dom = "indexer"
@@ -201,6 +247,9 @@ def main():
         "stages_ms": stage_ms,
         "step_bytes": total_bytes,
         "step_hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "copy_GBps": copy_gbs,
+        "timing": f"HIP graph replays: one graph per cache copy per step; stage times from graphs of "
+                  f"{reps} launches of one entry point",
         "rows_per_s": R * 1000.0 / ms,
     }
     if not args.no_cpu_baseline:
