@@ -18,9 +18,11 @@
 // Work balance: the pages of all sequences form one list; every workgroup
 // rebuilds its prefix sum in LDS and each wave takes an equal contiguous run
 // of it (so the grid depends only on host hints and no wave sits idle on
-// a short sequence).  The next page's K tile and scale are loaded while the
-// current page is multiplied.  HBM traffic per page: 8 KB codes + 256 B
-// scales, read once, coalesced 16-byte loads.
+// a short sequence).  A wave looks up the physical ids of up to 64 pages of
+// its run with one lane-parallel block-table load, and keeps the K tiles of
+// its next three pages in flight in a register ring while it multiplies the
+// current one.  HBM traffic per page: 8 KB codes + 256 B scales, read once,
+// coalesced 16-byte loads.
 #include "common.h"
 #include "kernels.h"
 
@@ -133,17 +135,28 @@ __device__ __forceinline__ void load_qrow(QRow& t, const uint8_t* q, const float
 
 // sum_h w_h * relu(q_h . k_s) for token `lane` of the page (before the K scale).
 __device__ __forceinline__ float page_row_logit(const QRow& qr, const KTile& kt, int lane) {
+  // The four products of a token tile are issued before any is consumed (and
+  // the next tile's before this tile's epilogue), so no product waits alone
+  // for the MFMA latency.
   float part[4];
+  v4f acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+    acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qr.q[mt], kt.k[0], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                  0, 0, 0, 0, 0, 0);
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
+    if (nt + 1 < 4) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        acc[(nt + 1) & 1][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            qr.q[mt], kt.k[nt + 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    }
     float s = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qr.q[mt], kt.k[nt], acc, 0, 0, 0, 0, 0, 0);
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(qr.w[mt][i], fmaxf(acc[i], 0.f), s);
-    }
+      for (int i = 0; i < 4; ++i) s = fmaf(qr.w[mt][i], fmaxf(acc[nt & 1][mt][i], 0.f), s);
     part[nt] = s;
   }
   // Reduce-scatter over the 4 lane groups g = lane >> 4 (each holds 16 of the
@@ -171,36 +184,50 @@ __global__ void __launch_bounds__(256) indexer_paged_kernel(PagedArgs a) {
   const int total = s_pref[B];
   const int64_t nw = (int64_t)gridDim.x * 4;
   const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int p = (int)((int64_t)total * gw / nw);
+  const int p_begin = (int)((int64_t)total * gw / nw);
   const int p_end = (int)((int64_t)total * (gw + 1) / nw);
-  if (p >= p_end) return;
+  if (p_begin >= p_end) return;
 
-  int b = find_seq(s_pref, B, p);
-  int seq_begin = s_pref[b], seq_end = s_pref[b + 1];
-
-  // Physical page of list position p (an out-of-range id comes back as -1).
-  auto phys_page = [&](int pp, int bb, int sb) -> int {
-    const int j = pp - sb;
-    const int id = a.batch.block_table[(int64_t)bb * a.batch.bt_stride + j];
-    return (id >= 0 && id < a.batch.num_pages) ? id : -1;
+  // Page table of up to 64 pages of this wave's run, one page per lane: its
+  // sequence, its page index inside the sequence and its physical page (-1
+  // when out of range).  One lane-parallel block-table load replaces a
+  // dependent load per page.
+  int pb = -1, lb = 0, lj = 0, lid = -1;
+  auto load_batch = [&](int first) {
+    pb = first;
+    const int p = first + lane;
+    lb = 0; lj = 0; lid = -1;
+    if (p < p_end) {
+      lb = find_seq(s_pref, B, p);
+      lj = p - s_pref[lb];
+      const int id = a.batch.block_table[(int64_t)lb * a.batch.bt_stride + lj];
+      lid = (id >= 0 && id < a.batch.num_pages) ? id : -1;
+    }
+  };
+  // K tiles of the next kRing pages stay in flight (a register ring); each
+  // slot keeps its page's id, sequence and page index, so reloading the page
+  // table for later pages never disturbs a pending slot.
+  constexpr int kRing = QL == 1 ? 2 : 1;
+  KTile kt[kRing];
+  int m_id[kRing], m_b[kRing], m_j[kRing];
+  auto issue = [&](int slot, int p) {
+    if (p < p_end) {
+      if (p - pb >= 64) load_batch(p);
+      m_id[slot] = __builtin_amdgcn_readlane(lid, p - pb);
+      m_b[slot] = __builtin_amdgcn_readlane(lb, p - pb);
+      m_j[slot] = __builtin_amdgcn_readlane(lj, p - pb);
+      if (m_id[slot] >= 0) load_ktile(kt[slot], a.cache + (int64_t)m_id[slot] * a.page_stride, lane);
+    }
   };
 
-  KTile cur, nxt;
-  int cur_page = phys_page(p, b, seq_begin);
-  if (cur_page >= 0) load_ktile(cur, a.cache + (int64_t)cur_page * a.page_stride, lane);
-
   QRow qr[QL];
-  int row0 = 0, nrows = 0, L = 0, q_len = 0, q0 = 0;
-  bool need_seq = true;
+  int cur_b = -1, row0 = 0, nrows = 0, L = 0, q_len = 0, q0 = 0;
 
-  for (; p < p_end; ++p) {
-    if (p >= seq_end) {  // crossed into the next sequence with pages
-      do { ++b; } while (s_pref[b + 1] <= p);
-      seq_begin = s_pref[b];
-      seq_end = s_pref[b + 1];
-      need_seq = true;
-    }
-    if (need_seq) {
+  auto compute = [&](int slot) {
+    const KTile& t = kt[slot];
+    const int id = m_id[slot], b = m_b[slot], j = m_j[slot];
+    if (b != cur_b) {
+      cur_b = b;
       q0 = a.batch.query_start[b];
       const int q1 = a.batch.query_start[b + 1];
       q_len = q1 - q0;
@@ -209,43 +236,25 @@ __global__ void __launch_bounds__(256) indexer_paged_kernel(PagedArgs a) {
       L = clamp_len(a.batch.seq_lens[b], a.batch.max_seq_len);
       if (nrows <= QL) {
 #pragma unroll
-        for (int j = 0; j < QL; ++j)
-          if (j < nrows) load_qrow(qr[j], a.q, a.w, row0 + j, lane);
+        for (int jj = 0; jj < QL; ++jj)
+          if (jj < nrows) load_qrow(qr[jj], a.q, a.w, row0 + jj, lane);
       }
-      need_seq = false;
     }
-    // prefetch the next page of this wave's run
-    int nxt_page = -1;
-    if (p + 1 < p_end) {
-      int nb = b, ns = seq_begin;
-      if (p + 1 >= seq_end) {
-        do { ++nb; } while (s_pref[nb + 1] <= p + 1);
-        ns = s_pref[nb];
-      }
-      nxt_page = phys_page(p + 1, nb, ns);
-      if (nxt_page >= 0) load_ktile(nxt, a.cache + (int64_t)nxt_page * a.page_stride, lane);
-    }
-
-    const int s = (p - seq_begin) * kPage + lane;  // logical token of this lane
+    const int s = j * kPage + lane;  // logical token of this lane
     const bool in_stride = s < a.logits_stride;
     for (int g0 = 0; g0 < nrows; g0 += QL) {
       if (nrows > QL) {
 #pragma unroll
-        for (int j = 0; j < QL; ++j)
-          if (g0 + j < nrows) load_qrow(qr[j], a.q, a.w, row0 + g0 + j, lane);
+        for (int jj = 0; jj < QL; ++jj)
+          if (g0 + jj < nrows) load_qrow(qr[jj], a.q, a.w, row0 + g0 + jj, lane);
       }
 #pragma unroll
-      for (int j = 0; j < QL; ++j) {
-        if (g0 + j >= nrows) break;
-        const int r = row0 + g0 + j;
+      for (int jj = 0; jj < QL; ++jj) {
+        if (g0 + jj >= nrows) break;
+        const int r = row0 + g0 + jj;
         int e = L - q_len + (r - q0) + 1;
         e = e < 0 ? 0 : e;
-        float v;
-        if (cur_page >= 0) {
-          v = page_row_logit(qr[j], cur, lane) * cur.scale;
-        } else {
-          v = -INFINITY;
-        }
+        const float v = id >= 0 ? page_row_logit(qr[jj], t, lane) * t.scale : -INFINITY;
         float* dst = a.logits + (int64_t)r * a.logits_stride + s;
         if (s < e) {
           if (in_stride) *dst = v;
@@ -254,8 +263,19 @@ __global__ void __launch_bounds__(256) indexer_paged_kernel(PagedArgs a) {
         }
       }
     }
-    cur = nxt;
-    cur_page = nxt_page;
+  };
+
+  load_batch(p_begin);
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) issue(i, p_begin + i);
+  for (int p = p_begin; p < p_end; p += kRing) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      if (p + i < p_end) {
+        compute(i);
+        issue(i, p + i + kRing);
+      }
+    }
   }
 }
 
