@@ -85,6 +85,7 @@ INDEXER_CASES = {
     "qlen_ge_len": ([5, 300, 3], [5, 3, 7], {}),
     "padded_pages": ([1000, 333], [1, 3], {"idx_page_pad": 512}),
     "prefill_rows": ([2600], [200], {}),
+    "prefill_chunks": ([9000, 5000, 64], [300, 17, 9], {}),
     "many_seqs": (list(range(1, 400, 7)), [1] * 57, {}),
 }
 
