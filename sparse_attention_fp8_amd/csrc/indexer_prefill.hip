@@ -8,18 +8,21 @@
 // contraction (16384 flop per (row, key)) and the MFMA rate is the bound.
 //
 // gfx950 design.
-//  * Workgroup = 8 query rows of one sequence x a chunk of 4096 keys; one wave
-//    per row.  The wave keeps its row's q (64 heads x 128 e4m3) in registers
-//    as the A operand of v_mfma_f32_32x32x64_f8f6f4 (M = 32 heads, N = 32
-//    keys, K = 64; 4 instructions per 32 keys), the fastest fp8 shape on this
-//    chip.  The C layout gives each lane 16 heads of one key, so the weighted
-//    ReLU head sum is 32 in-lane FMAs plus one cross-lane add.
-//  * K arrives in stages of 128 keys (two 64-token pages, located through the
-//    block table): every wave loads 2 KB of a stage into registers two stages
-//    ahead and writes it to a double-buffered LDS tile, where key n's 16-byte
-//    chunk c sits in slot c ^ (n & 7) of its 128-byte row: the B-operand reads
-//    of 8 consecutive keys then hit distinct bank groups.  All 8 rows share
-//    each K tile, so a stage costs one 17 KB global read per 8 MB of flops.
+//  * Workgroup = 16 query rows of one sequence x a chunk of 4096 keys; each of
+//    the 8 waves owns two rows and keeps their q (64 heads x 128 e4m3 each) in
+//    registers as A operands of v_mfma_f32_32x32x64_f8f6f4 (M = 32 heads,
+//    N = 32 keys, K = 64; 4 instructions per row and 32 keys), the fastest
+//    fp8 shape on this chip.  One B-operand read of 32 keys feeds both rows.
+//  * The C layout gives each lane 16 heads of one key, so the weighted ReLU
+//    head sum is 32 in-lane FMAs (ReLU as one v_med3_f32) plus one lane swap
+//    (v_permlane32_swap).  This epilogue, two VALU operations per (row, key,
+//    head), costs about as much issue time as the MFMAs and bounds the kernel.
+//  * K arrives in stages of 256 keys (four 64-token pages, located through the
+//    block table), copied global->LDS (global_load_lds_dwordx4, one whole
+//    128-byte key row per 8 lanes) into a double-buffered tile where key n's
+//    16-byte chunk c sits in slot c ^ ((n >> 1) & 7) of its row: the B-operand
+//    reads of 16 consecutive keys then hit distinct banks.  The copy of stage
+//    s + 1 is in flight while stage s is multiplied.
 //  * Workgroup ids run over the key chunks fastest, so the 8 XCDs each serve
 //    two key chunks from their own L2 to every row block.
 //  * Keys s >= e_r are masked (written -inf when clean_logits); chunks cover
@@ -31,15 +34,43 @@ namespace dsa {
 
 namespace {
 
-constexpr int kRowsPerBlock = 8;                 // one row per wave
-constexpr int kThreadsPf = 64 * kRowsPerBlock;
+constexpr int kWavesPf = 8;
+constexpr int kRowsPerWave = 2;
+constexpr int kRowsPerBlock = kWavesPf * kRowsPerWave;   // 16 query rows per workgroup
+constexpr int kThreadsPf = 64 * kWavesPf;
 constexpr int kChunkKeys = 4096;                 // keys per workgroup
-constexpr int kStageKeys = 128;                  // keys per LDS stage (two pages)
-constexpr int kStagesPerChunk = kChunkKeys / kStageKeys;
+constexpr int kStageKeys = 256;                  // keys per LDS stage (four pages)
 constexpr int kPagesPerChunk = kChunkKeys / kPage;
-constexpr int kStageCodeBytes = kStageKeys * kIdxDim;   // 16 KB
+constexpr int kStageCodeBytes = kStageKeys * kIdxDim;    // 32 KB
+constexpr int kDmaPerWave = kStageCodeBytes / 1024 / kWavesPf;   // 1 KB copies per wave and stage
+constexpr int kScaleWaves = kStageKeys / kPage;          // waves that also copy one page's scales
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Slot swizzle of key row n (128 bytes): 16 lanes of a 128-bit LDS access are
+// served per cycle from 256 bytes of banks, so the 16 key rows one B-operand
+// read touches must land on 16 distinct 16-byte units modulo 256 -- row parity
+// times the slot XORed with (n >> 1) & 7 does that.
+__device__ __forceinline__ int swz(int n) { return (n >> 1) & 7; }
+
+// max(x, 0) in one instruction (v_med3_f32 with 0 and the largest float):
+// fmaxf() adds a NaN-quieting max in front of every use, which doubles the
+// epilogue's VALU work (inputs here are finite fp8 dot products).
+__device__ __forceinline__ float relu1(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds
+// wave-uniform).  Inline asm: the compiler would otherwise make every later
+// LDS read wait for the copy; the kernel waits (vmcnt) before its barrier.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+
+// Source of rows and scales of pages the chunk does not have.
+__device__ __attribute__((aligned(16))) uint32_t g_zero_kv[64] = {};
 
 struct PrefillArgs {
   BatchArgs batch;
@@ -50,7 +81,7 @@ struct PrefillArgs {
   float* logits;
   int64_t logits_stride;
   int clean;
-  int row_blocks;   // ceil(max_q_len / 8)
+  int row_blocks;   // ceil(max_q_len / 16)
   int key_chunks;   // ceil(logits_stride / 4096)
 };
 
@@ -60,17 +91,12 @@ struct PrefillShared {
   int page[kPagesPerChunk];                  // physical page of each page of the chunk (-1: none)
 };
 
-// Stage data a wave carries from global memory to LDS: the codes of keys
-// 16 w .. 16 w + 15 and, for waves 0 and 1, the 64 scales of one page.
-struct StageRegs {
-  v4i c[2];
-  float s;
+// One query row of a wave: q as MFMA A operands and the head weights of the
+// lane's C-layout heads.
+struct RowOperands {
+  v8i qa[2][2];      // [head tile][K half]
+  float wr[2][16];   // [head tile][C item]
 };
-
-__device__ __forceinline__ v4i load16_or_zero(const uint8_t* p, bool ok) {
-  v4i z = {0, 0, 0, 0};
-  return ok ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(p)) : z;
-}
 
 __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs a) {
   __shared__ PrefillShared sh;
@@ -114,60 +140,61 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
   }
   __syncthreads();
 
-  // Loads of stage st: wave w copies keys 16 w .. 16 w + 15 (2 KB) in two
-  // loads; in load j lane l takes chunk l % 8 of key 16 w + 8 j + l / 8, so
-  // every 8 lanes read one whole 128-byte key row.  Waves 0 and 1 also take
-  // the 64 scales of page 2 st + w.
-  auto load_stage = [&](StageRegs& R, int st) {
+  // Copy of stage st into buffer buf: wave w fills 1 KB blocks w * kDmaPerWave
+  // + i (8 key rows each); lane l fills slot l % 8 of row l / 8 of the block
+  // with chunk (l % 8) ^ swz(row), so every 8 lanes read one whole 128-byte
+  // key row.  The first kScaleWaves waves also copy one page's 256 scale bytes
+  // (lanes 0-15).
+  auto copy_stage = [&](int st, int buf) __attribute__((always_inline)) {
+    const uint32_t dst = lds_addr(sh.codes[buf]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = st * kStageKeys + 16 * wave + 8 * j + (lane >> 3);   // key within the chunk
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int blk = wave * kDmaPerWave + i;
+      const int n = 8 * blk + (lane >> 3);              // key row within the stage
+      const int key = st * kStageKeys + n;              // key within the chunk
       const int id = sh.page[key >> 6];
-      const bool ok = id >= 0;
-      const uint8_t* row = a.cache + (int64_t)(ok ? id : 0) * a.page_stride + (key & 63) * kIdxDim;
-      R.c[j] = load16_or_zero(row + 16 * (lane & 7), ok);
+      const int c = (lane & 7) ^ swz(n);
+      const unsigned char* src = id >= 0
+          ? a.cache + (int64_t)id * a.page_stride + (key & 63) * kIdxDim + 16 * c
+          : reinterpret_cast<const unsigned char*>(g_zero_kv) + 16 * c;
+      lds_dma16(src, dst + blk * 1024);
     }
-    R.s = 0.f;
-    if (wave < 2) {
-      const int pid = sh.page[2 * st + wave];
-      if (pid >= 0)
-        R.s = __builtin_nontemporal_load(reinterpret_cast<const float*>(a.cache + (int64_t)pid * a.page_stride +
-                                                                          kIdxScaleOff) + lane);
+    if (wave < kScaleWaves && lane < 16) {
+      const int id = sh.page[kScaleWaves * st + wave];
+      const unsigned char* src = id >= 0 ? a.cache + (int64_t)id * a.page_stride + kIdxScaleOff + 16 * lane
+                                         : reinterpret_cast<const unsigned char*>(g_zero_kv) + 16 * lane;
+      lds_dma16(src, lds_addr(&sh.scales[buf][kPage * wave]));
     }
-  };
-  auto write_stage = [&](const StageRegs& R, int buf) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = 16 * wave + 8 * j + (lane >> 3);
-      *reinterpret_cast<v4i*>(sh.codes[buf] + n * kIdxDim + 16 * ((lane & 7) ^ (n & 7))) = R.c[j];
-    }
-    if (wave < 2) sh.scales[buf][64 * wave + lane] = R.s;
   };
 
-  // This wave's row: q as A operands (head 32 mt + l % 32, bytes
-  // 64 j + 32 (l / 32) .. +32) and the weights of the 16 heads each lane
-  // holds per head tile in the C layout (head 32 mt + (i % 4) + 4 (l / 32) +
-  // 8 (i / 4) for item i).
-  const bool has_row = wave < nrows;
-  const int r = row0 + (has_row ? wave : 0);
-  const int e_r = has_row ? extent(r) : 0;
-  v8i qa[2][2];
-  float wr[2][16];
-  {
-    const int hq = lane & 31, hk = lane >> 5;
+  // This wave's rows row0 + wave and row0 + wave + 8: q as A operands (head
+  // 32 mt + l % 32, bytes 64 j + 32 (l / 32) .. +32) and the weights of the
+  // 16 heads each lane holds per head tile in the C layout (head 32 mt +
+  // (i % 4) + 4 (l / 32) + 8 (i / 4) for item i).
+  const int hq = lane & 31, hk = lane >> 5;
+  RowOperands ro[kRowsPerWave];
+  bool has_row[kRowsPerWave];
+  int rr[kRowsPerWave], e_r[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int ri = wave + kWavesPf * j;   // rows of the block, wave-major
+    has_row[j] = ri < nrows;
+    rr[j] = row0 + (has_row[j] ? ri : 0);
+    e_r[j] = has_row[j] ? extent(rr[j]) : 0;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const uint8_t* qp = a.q + ((int64_t)r * kIdxHeads + 32 * mt + hq) * kIdxDim + 32 * hk;
+      const uint8_t* qp = a.q + ((int64_t)rr[j] * kIdxHeads + 32 * mt + hq) * kIdxDim + 32 * hk;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(qp + 64 * j);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(qp + 64 * j + 16);
-        qa[mt][j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      for (int kh = 0; kh < 2; ++kh) {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(qp + 64 * kh);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(qp + 64 * kh + 16);
+        ro[j].qa[mt][kh] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 ww = *reinterpret_cast<const float4*>(a.w + (int64_t)r * kIdxHeads + 32 * mt + 8 * g + 4 * hk);
-        wr[mt][4 * g] = ww.x; wr[mt][4 * g + 1] = ww.y; wr[mt][4 * g + 2] = ww.z; wr[mt][4 * g + 3] = ww.w;
+        const float4 ww = *reinterpret_cast<const float4*>(a.w + (int64_t)rr[j] * kIdxHeads + 32 * mt + 8 * g + 4 * hk);
+        ro[j].wr[mt][4 * g] = ww.x; ro[j].wr[mt][4 * g + 1] = ww.y;
+        ro[j].wr[mt][4 * g + 2] = ww.z; ro[j].wr[mt][4 * g + 3] = ww.w;
       }
     }
   }
@@ -179,62 +206,72 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int chunk = (c < 2 ? 2 * hb + c : 4 + 2 * hb + (c - 2));
-    boff[c] = nb * kIdxDim + 16 * (chunk ^ (nb & 7));
+    boff[c] = nb * kIdxDim + 16 * (chunk ^ swz(nb));
   }
 
-  auto compute_stage = [&](int st, int buf) {
-    const int skey0 = key0 + st * kStageKeys;
+  // Epilogue of one row and 32 keys: weighted ReLU head sum (in-lane over the
+  // lane's 32 heads, then lanes 0-31 add lanes 32-63 with a lane swap), K
+  // scale, masked store.
+  auto epilogue = [&](const RowOperands& o, const v16f* acc, int row, int er, bool hr, int key, float scale)
+      __attribute__((always_inline)) {
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int step = 0; step < kStageKeys / 32; ++step) {
-      const unsigned char* tb = sh.codes[buf] + step * 32 * kIdxDim;
-      v8i bop[2];
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const v4i x0 = *reinterpret_cast<const v4i*>(tb + boff[2 * j]);
-        const v4i x1 = *reinterpret_cast<const v4i*>(tb + boff[2 * j + 1]);
-        bop[j] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      }
-      v16f acc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        v16f z;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = 0.f;
-        acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][0], bop[0], z, 0, 0, 0, 0, 0, 0);
-        acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[mt][1], bop[1], acc[mt], 0, 0, 0, 0, 0, 0);
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s = fmaf(wr[mt][i], fmaxf(acc[mt][i], 0.f), s);
-      s += __shfl_xor(s, 32, 64);
-      const int key = skey0 + step * 32 + nb;
-      const float v = s * sh.scales[buf][step * 32 + nb];
-      if (has_row && hb == 0 && key < key_end) {
-        float* dst = a.logits + (int64_t)r * a.logits_stride + key;
-        if (key < e_r) *dst = v;
-        else if (a.clean) *dst = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i) p[i & 3] = fmaf(o.wr[mt][i], relu1(acc[mt][i]), p[i & 3]);
+    float s = (p[0] + p[1]) + (p[2] + p[3]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s += __uint_as_float(sw[1]);
+    const float v = s * scale;
+    if (hr && hb == 0 && key < key_end) {
+      float* dst = a.logits + (int64_t)row * a.logits_stride + key;
+      if (key < er) *dst = v;
+      else if (a.clean) *dst = -INFINITY;
     }
   };
 
-  // Two register sets carry stages two ahead of the LDS buffers.
-  StageRegs R0, R1;
-  load_stage(R0, 0);
-  if (nstages > 1) load_stage(R1, 1);
-  write_stage(R0, 0);
-  __syncthreads();
-  for (int st = 0; st < nstages; st += 2) {
-    if (st + 2 < nstages) load_stage(R0, st + 2);
-    compute_stage(st, 0);
-    if (st + 1 < nstages) write_stage(R1, 1);
-    __syncthreads();
-    if (st + 1 >= nstages) break;
-    if (st + 3 < nstages) load_stage(R1, st + 3);
-    compute_stage(st + 1, 1);
-    if (st + 2 < nstages) write_stage(R0, 0);
-    __syncthreads();
+  auto compute_stage = [&](int st, int buf) __attribute__((always_inline)) {
+    constexpr int kSteps = kStageKeys / 32;
+#pragma unroll 2
+    for (int step = 0; step < kSteps; ++step) {
+      const unsigned char* tb = sh.codes[buf] + step * 32 * kIdxDim;
+      v8i bop[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const v4i x0 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh]);
+        const v4i x1 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh + 1]);
+        bop[kh] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+      const float scale = sh.scales[buf][step * 32 + nb];
+      v16f z;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) z[i] = 0.f;
+      v16f acc[kRowsPerWave][2];
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[mt][0], bop[0], z, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[mt][1], bop[1], acc[j][mt],
+                                                                       0, 0, 0, 0, 0, 0);
+      const int key = key0 + st * kStageKeys + step * 32 + nb;
+#pragma unroll
+      for (int j = 0; j < kRowsPerWave; ++j) epilogue(ro[j], acc[j], rr[j], e_r[j], has_row[j], key, scale);
+    }
+  };
+
+  // Double-buffered stages: the copy of stage st + 1 is in flight while stage
+  // st is multiplied; each wave waits for its own copies before the barrier.
+  copy_stage(0, 0);
+  for (int st = 0; st < nstages; ++st) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();            // stage st landed; buffer (st + 1) & 1 is free
+    if (st + 1 < nstages) copy_stage(st + 1, (st + 1) & 1);
+    compute_stage(st, st & 1);
   }
 }
 
