@@ -72,6 +72,36 @@ def _row_extents(seq_lens, qs):
     return seq, ext
 
 
+STAGE_SOURCES = {"indexer": "indexer_paged.hip", "indexer_prefill": "indexer_prefill.hip",
+                 "topk": "topk.hip", "sparse_mla": "sparse_mla.hip"}
+
+
+def stage_source_sha(stage):
+    """sha256 prefix of the kernel sources of one stage (its file + common.h)."""
+    import hashlib
+    m = hashlib.sha256()
+    for f in (STAGE_SOURCES[stage], "common.h"):
+        with open(os.path.join(ROOT, "sparse_attention_fp8_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
+def measured_traffic(config, stage):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 PMC summary of
+    this workload, or None when there is none or the stage's sources changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"dsa_step_{config}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    want = stage_source_sha(stage)
+    with open(path) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 4 and parts[0] == "traffic:" and parts[1] == stage and parts[2] == want:
+                return int(parts[3])
+    return None
+
+
 def cpu_baseline(wl, budget_s):
     """Time the float64 oracle on a bounded, seeded sample of the step's rows."""
     import oracle
@@ -220,13 +250,13 @@ def main():
         dom = "indexer"
         achieved = nbytes["indexer_flops"] / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": measured_traffic(args.config, "indexer_prefill"),
                 "kernel": "indexer_prefill", "per_launch": f"{nbytes['indexer_flops']} flop"}
     else:
         dom = max(stage_ms, key=stage_ms.get)
         achieved = nbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, dom), "kernel": dom,
                 "per_launch": f"{nbytes[dom]} B"}
     line = {
         "metric": "DSA decode steps/s (indexer+topk+sparse MLA) and % of HBM roofline at 1 GPU",
