@@ -141,16 +141,16 @@ __device__ __forceinline__ int block_scan(int v, Shared& sh) {
 // keys the k-th largest key is never 0 and a key-0 slot is never selected.
 // Wave w copies the V = KPT / 4 float4s of each of its lanes to LDS: owner
 // lane L's float4 j goes to slot L V + (j ^ swz(L)) of the wave's area, with
-// swz(L) = (L / (8 / V)) % V.  Eight consecutive lanes then read eight
-// distinct 16-byte bank groups, and each group of 8 lanes of one copy
-// instruction reads one whole 128-byte line.  Float4s at or past n are not
-// read (their slot gets a copy of the row's first float4 and is masked
-// afterwards); src is 16-byte aligned and every float4 that starts below n
-// lies inside the row.
+// swz(L) = (L / (16 / V)) % V.  The 16 lanes a 128-bit LDS read serves per
+// cycle then hit 16 distinct 16-byte units modulo 256 bytes of banks, and each
+// group of 8 lanes of one copy instruction reads one whole 128-byte line.
+// Float4s at or past n are not read (their slot gets a copy of the row's first
+// float4 and is masked afterwards); src is 16-byte aligned and every float4
+// that starts below n lies inside the row.
 template <int KPT>
 __device__ void load_keys(Keys<KPT>& keys, const float* src, int n, float4* stage) {
   constexpr int V = KPT / 4;
-  constexpr int F = 8 / V;
+  constexpr int F = 16 / V;
   const int w = threadIdx.x >> 6, l = lane_id();
   const float4* src4 = reinterpret_cast<const float4*>(src);
   float4* wst = stage + w * 64 * V;

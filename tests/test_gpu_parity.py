@@ -340,3 +340,26 @@ def test_full_step_small(dsa):
     out, lse = run_mla(dsa, wl, batch, t, idx, 0)
     o_ref, l_ref = mla_oracle(wl, idx)
     check_mla(out, lse, o_ref, l_ref, "step")
+
+
+def test_sparse_mla_workspace_reused_across_calls(dsa):
+    """One workspace, never initialised (random bytes), serves consecutive split
+    calls of different shapes: the arrival counters are tagged per call."""
+    wa = synth.make_workload([5000, 3000, 130], [1, 1, 2], 32, seed=21, spare_pages=3, poison=True)
+    wb = synth.make_workload([9000], [1], 32, seed=22, spare_pages=3, poison=True)
+    ia = np.stack([np.sort(np.random.default_rng(r).choice(max(e, 1), size=2048, replace=e < 2048))
+                   for r, e in enumerate(oracle.row_extents(wa.seq_lens.numpy(), wa.query_start.numpy())[1])]).astype(np.int32)
+    ib = np.sort(np.random.default_rng(9).choice(9000, size=2048, replace=False))[None].astype(np.int32)
+    ba, ta = to_dev(wa)
+    bb, tb = to_dev(wb)
+    need = max(dsa.sparse_mla_workspace_bytes(ba, 32, 2048, 8), dsa.sparse_mla_workspace_bytes(bb, 32, 2048, 3))
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, generator=torch.Generator().manual_seed(5)).to(DEV)
+    for wl, batch, t, idx, splits in ((wa, ba, ta, ia, 8), (wb, bb, tb, ib, 3), (wa, ba, ta, ia, 8), (wb, bb, tb, ib, 32)):
+        R, H = wl.num_rows, wl.num_heads
+        out = torch.full((R, H, 512), float("nan"), dtype=torch.bfloat16, device=DEV)
+        lse = torch.full((R, H), float("nan"), dtype=torch.float32, device=DEV)
+        dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], torch.from_numpy(idx).to(DEV), wl.softmax_scale,
+                              out, lse, num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, l_ref = mla_oracle(wl, idx)
+        check_mla(out, lse, o_ref, l_ref, f"reused workspace, splits={splits}")
