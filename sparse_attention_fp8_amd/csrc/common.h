@@ -118,6 +118,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// x from lane l ^ 32 / l ^ 16 through the VALU lane-swap instructions (no LDS
+// round trip).  permlane32_swap exchanges the upper half of its first operand
+// with the lower half of its second; permlane16_swap the odd 16-lane rows of
+// the first with the even rows of the second.
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+}
+__device__ __forceinline__ float lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((lane_id() & 16) ? r[0] : r[1]);
+}
+
+// max(x, 0) in one instruction (v_med3_f32 with 0 and the largest float) for
+// finite inputs such as MFMA results; fmaxf() adds a NaN-quieting max first.
+__device__ __forceinline__ float relu_finite(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
+
 // bf16 helpers (bit patterns in uint16 / packed pairs in uint32).
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }

@@ -156,7 +156,7 @@ __device__ __forceinline__ float page_row_logit(const QRow& qr, const KTile& kt,
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(qr.w[mt][i], fmaxf(acc[nt & 1][mt][i], 0.f), s);
+      for (int i = 0; i < 4; ++i) s = fmaf(qr.w[mt][i], relu_finite(acc[nt & 1][mt][i]), s);
     part[nt] = s;
   }
   // Reduce-scatter over the 4 lane groups g = lane >> 4 (each holds 16 of the
@@ -166,11 +166,11 @@ __device__ __forceinline__ float page_row_logit(const QRow& qr, const KTile& kt,
   const bool hi = g >= 2;
   float send0 = hi ? part[0] : part[2];
   float send1 = hi ? part[1] : part[3];
-  float a0 = (hi ? part[2] : part[0]) + __shfl_xor(send0, 32, 64);
-  float a1 = (hi ? part[3] : part[1]) + __shfl_xor(send1, 32, 64);
+  float a0 = (hi ? part[2] : part[0]) + lane_xor32(send0);
+  float a1 = (hi ? part[3] : part[1]) + lane_xor32(send1);
   const bool odd = g & 1;
   float send = odd ? a0 : a1;
-  return (odd ? a1 : a0) + __shfl_xor(send, 16, 64);
+  return (odd ? a1 : a0) + lane_xor16(send);
 }
 
 template <int QL>

@@ -53,11 +53,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // times the slot XORed with (n >> 1) & 7 does that.
 __device__ __forceinline__ int swz(int n) { return (n >> 1) & 7; }
 
-// max(x, 0) in one instruction (v_med3_f32 with 0 and the largest float):
-// fmaxf() adds a NaN-quieting max in front of every use, which doubles the
-// epilogue's VALU work (inputs here are finite fp8 dot products).
-__device__ __forceinline__ float relu1(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.402823466e38f); }
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -218,7 +213,7 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i & 3] = fmaf(o.wr[mt][i], relu1(acc[mt][i]), p[i & 3]);
+      for (int i = 0; i < 16; ++i) p[i & 3] = fmaf(o.wr[mt][i], relu_finite(acc[mt][i]), p[i & 3]);
     float s = (p[0] + p[1]) + (p[2] + p[3]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
     s += __uint_as_float(sw[1]);
