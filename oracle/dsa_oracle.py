@@ -32,6 +32,12 @@ What it computes, and where each step comes from:
   single-pass fast path, and -1e30 as the running-max sentinel of fully masked
   tiles.  Score z = scale * q[h, :576] . c[s, :576]; value = c[s, :512];
   out = softmax(z) @ V; lse = ln sum exp(z) (natural log).
+* Quantisation and cache writes (the steps before the path).  The
+  vllm-dsa-mtp-sm80 README (skew fixes 0 and 1) names the indexer-K cache
+  writer and the per-token-group fp8 quantiser of the indexer q; the reading of
+  their arithmetic (one amax / 448 scale per 128 values, round-to-nearest-even
+  saturating e4m3fn codes, decided in fp32) is stated where they are written
+  out, with the bf16 latent-cache writer beside them.
 """
 from __future__ import annotations
 
@@ -285,3 +291,94 @@ def sparse_mla_split(q_mla, kv_cache, block_table, seq_lens, query_start, indice
         out[o][ok] = A[ok] / L[ok][:, None]
         lse[o][ok] = M[ok] + np.log(L[ok])
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# quantisation and cache writes: the steps just before the path
+#
+# The vllm-dsa-mtp-sm80 README names them (skew fix 0: indexer_k_quant_and_cache
+# writes the paged indexer K through the page stride; skew fix 1: the unfused
+# per_token_group_quant_fp8 quantises the indexer q).  The pages print neither
+# body.  The reading taken: one fp32 scale per 128-value group (a K token, or
+# one (row, head) of q), scale = amax / 448 so the largest element lands on
+# the largest finite e4m3fn value, codes = e4m3fn(x / scale) rounded to nearest
+# with ties to the even code and saturated at +-448; an all-zero group takes
+# scale 1.  Every fp32 step (amax, the scale division, x / scale) is taken in
+# IEEE fp32, the precision the codes are decided in.  The q scale is folded
+# into the indexer head weight: w'[r, h] = fp32(w[r, h] * scale[r, h]).
+
+E4M3_MAX = 448.0
+_E4M3_GRID = e4m3fn_decode(np.arange(127, dtype=np.uint8))   # codes 0x00..0x7E, ascending
+
+
+def e4m3fn_encode(y) -> np.ndarray:
+    """float -> OCP E4M3 code: nearest representable value, ties to the even
+    code (even mantissa), |y| > 448 saturating to +-448, sign kept (so -0 and
+    negative values that round to zero give 0x80).  NaN gives 0x7F / 0xFF."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    lo = np.clip(np.searchsorted(_E4M3_GRID, a, side="right") - 1, 0, 126)
+    hi = np.minimum(lo + 1, 126)
+    d_lo = a - _E4M3_GRID[lo]
+    d_hi = _E4M3_GRID[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.int64)
+    code = np.where(np.isnan(y), 0x7F, code)
+    return (code | (np.signbit(y).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_groups_fp8(x_bf16):
+    """bf16 bit patterns [..., 128] -> (e4m3fn codes [..., 128], fp32 scales [...])."""
+    x = bf16_decode(x_bf16).astype(np.float32)          # exact
+    amax = np.max(np.abs(x), axis=-1)                    # exact
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)        # IEEE fp32 division
+    return e4m3fn_encode(y), scale
+
+
+def indexer_q_quant(q_bf16, weights):
+    """Indexer q quantisation: q [R, 64, 128] bf16 bits and w [R, 64] fp32 ->
+    (codes [R, 64, 128] uint8, w' [R, 64] fp32 with the q scale folded in)."""
+    codes, scale = quantize_groups_fp8(np.asarray(q_bf16))
+    w = np.asarray(weights, dtype=np.float32)
+    return codes, (w * scale).astype(np.float32)
+
+
+def _slot_targets(slot_mapping, num_pages):
+    """(token, page, slot-in-page) of every token whose slot lands in the cache.
+
+    slot = page * 64 + slot-in-page; a negative slot (a padding token) or one on
+    a page outside [0, num_pages) writes nothing."""
+    sm = np.asarray(slot_mapping, dtype=np.int64)
+    ok = (sm >= 0) & (sm < np.int64(num_pages) * PAGE)
+    t = np.nonzero(ok)[0]
+    return t, sm[t] // PAGE, sm[t] % PAGE
+
+
+def indexer_k_quant_and_cache(k_bf16, slot_mapping, idx_cache):
+    """Quantise K [T, 128] bf16 bits per token and write it into a copy of the
+    paged indexer cache [num_pages, page_stride] uint8: codes at
+    page * stride + slot * 128, the fp32 scale at page * stride + 8192 + slot * 4.
+    Bytes of other slots, and the page padding, keep their value."""
+    cache = np.array(idx_cache, dtype=np.uint8, copy=True)
+    codes, scale = quantize_groups_fp8(np.asarray(k_bf16))
+    t, page, slot = _slot_targets(slot_mapping, cache.shape[0])
+    for i, p, s in zip(t, page, slot):
+        cache[p, s * IDX_DIM:(s + 1) * IDX_DIM] = codes[i]
+        cache[p, IDX_SCALE_OFFSET + 4 * s:IDX_SCALE_OFFSET + 4 * s + 4] = \
+            np.frombuffer(np.float32(scale[i]).tobytes(), dtype=np.uint8)
+    return cache
+
+
+def latent_cache_write(latent_bf16, rope_bf16, slot_mapping, kv_cache):
+    """Write each token's latent row [512] followed by its rope part [64] (bf16
+    bits, unchanged) into a copy of the paged latent cache [num_pages, stride]
+    at page * stride + slot * 576."""
+    cache = np.array(kv_cache, copy=True)
+    lat = np.asarray(latent_bf16)
+    rope = np.asarray(rope_bf16)
+    t, page, slot = _slot_targets(slot_mapping, cache.shape[0])
+    for i, p, s in zip(t, page, slot):
+        cache[p, s * KV_DIM:s * KV_DIM + V_DIM] = lat[i]
+        cache[p, s * KV_DIM + V_DIM:(s + 1) * KV_DIM] = rope[i]
+    return cache
