@@ -82,6 +82,7 @@ typedef enum {
 #define DSA_V_DIM 512
 #define DSA_MAX_TOPK 2048
 #define DSA_MAX_SEQS 4096
+#define DSA_MAX_WRITE_ITEMS (1 << 24) /* rows / tokens per quantiser or cache-writer call */
 
 /* One step's batch description, shared by all four calls. */
 typedef struct {
@@ -176,6 +177,71 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
                           const uint16_t* kv_cache, int64_t kv_page_stride, const int32_t* indices,
                           int32_t k, float softmax_scale, int32_t num_splits, uint16_t* out,
                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The steps just before the path: the indexer-q quantiser and the two cache
+ * writers (vllm-dsa-mtp-sm80 README, skew fixes 0 and 1, which name the
+ * unfused per_token_group_quant_fp8 for the indexer q and the indexer-K cache
+ * writer indexer_k_quant_and_cache that addresses pages through their stride).
+ * The pages do not print their arithmetic; the reading implemented is:
+ *   per group of 128 values x (one (row, head) of q, or one K token), in IEEE
+ *   fp32:  amax = max |x|;  scale = amax / 448, or 1 when amax == 0;
+ *          code = e4m3fn(x / scale), round to nearest even, saturating at
+ *          +-448 (so the largest element always lands on +-448), sign kept.
+ *   Results are bit-exact functions of the inputs (no reduction-order freedom).
+ * Non-finite inputs give unspecified codes and scales (but no fault).
+ *
+ * Slots: slot_mapping[t] = page * 64 + slot-in-page of token t (int64).  A
+ * negative slot (a padding token) or one >= num_pages * 64 writes nothing.
+ * Two tokens with the same slot in one call race: which one lands is
+ * unspecified.  Only the token's own bytes in its page are written; other
+ * slots and the page padding are never touched.
+ */
+
+/*
+ * dsa_indexer_q_quant_fp8 -- quantise the indexer q per (row, head) and fold
+ * the scale into the head weights, producing dsa_indexer_logits_*'s inputs.
+ *  q            [R, 64, 128] bf16, 16-byte aligned
+ *  weights      [R, 64] fp32 head weights, 4-byte aligned
+ *  q_fp8        [R, 64, 128] e4m3fn codes out, 8-byte aligned
+ *  weights_out  [R, 64] fp32 out: weights[r, h] * scale[r, h] (one fp32
+ *               multiply); may be the same buffer as `weights` (in place)
+ *  0 <= R <= DSA_MAX_WRITE_ITEMS.
+ */
+int dsa_indexer_q_quant_fp8(int32_t num_rows, const uint16_t* q, const float* weights, uint8_t* q_fp8,
+                            float* weights_out, void* stream);
+
+/*
+ * dsa_indexer_k_quant_and_cache -- quantise each new token's indexer K and
+ * write its 128 codes to page * idx_page_stride + slot * 128 and its fp32
+ * scale to page * idx_page_stride + 8192 + slot * 4 of idx_cache.
+ *  k             [T, k_stride] bf16 (first 128 used); k_stride >= 128 and a
+ *                multiple of 8 elements; 16-byte aligned
+ *  slot_mapping  [T] int64, 8-byte aligned (see "Slots" above)
+ *  idx_cache     indexer pages (layout above), 16-byte aligned;
+ *                idx_page_stride >= 8448 bytes, a multiple of 16
+ *  num_pages     pages in idx_cache
+ *  0 <= T <= DSA_MAX_WRITE_ITEMS.
+ */
+int dsa_indexer_k_quant_and_cache(int32_t num_tokens, const uint16_t* k, int64_t k_stride,
+                                  const int64_t* slot_mapping, uint8_t* idx_cache, int64_t idx_page_stride,
+                                  int32_t num_pages, void* stream);
+
+/*
+ * dsa_latent_cache_write -- copy each new token's latent row (512 bf16) and
+ * rope part (64 bf16) into its latent-cache slot, latent first, unchanged:
+ * kv_cache[page * kv_page_stride + slot * 576 + (0..575)].
+ *  latent  [T, latent_stride] bf16 (first 512 used), latent_stride >= 512
+ *  rope    [T, rope_stride] bf16 (first 64 used), rope_stride >= 64
+ *          (strides in elements, multiples of 8; both 16-byte aligned)
+ *  slot_mapping  [T] int64, 8-byte aligned (see "Slots" above)
+ *  kv_cache      latent pages, 16-byte aligned; kv_page_stride >= 36864
+ *                elements, a multiple of 8
+ *  0 <= T <= DSA_MAX_WRITE_ITEMS.
+ */
+int dsa_latent_cache_write(int32_t num_tokens, const uint16_t* latent, int64_t latent_stride, const uint16_t* rope,
+                           int64_t rope_stride, const int64_t* slot_mapping, uint16_t* kv_cache,
+                           int64_t kv_page_stride, int32_t num_pages, void* stream);
 
 /* Workspace sizes (host fields of `batch` only; 0 when none is needed). */
 size_t dsa_topk_workspace_bytes(const dsa_batch_t* batch, int32_t k);

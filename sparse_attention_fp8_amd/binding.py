@@ -63,6 +63,9 @@ def load():
         "dsa_indexer_logits_prefill": (ctypes.c_int, [B, vp, vp, vp, i64, vp, i64, ctypes.c_int, vp]),
         "dsa_topk": (ctypes.c_int, [B, vp, i64, i32, vp, vp, sz, vp]),
         "dsa_sparse_mla_decode": (ctypes.c_int, [B, vp, i32, vp, i64, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
+        "dsa_indexer_q_quant_fp8": (ctypes.c_int, [i32, vp, vp, vp, vp, vp]),
+        "dsa_indexer_k_quant_and_cache": (ctypes.c_int, [i32, vp, i64, vp, vp, i64, i32, vp]),
+        "dsa_latent_cache_write": (ctypes.c_int, [i32, vp, i64, vp, i64, vp, vp, i64, i32, vp]),
         "dsa_topk_workspace_bytes": (sz, [B, i32]),
         "dsa_sparse_mla_workspace_bytes": (sz, [B, i32, i32, i32]),
         "dsa_sparse_mla_pick_splits": (i32, [B, i32, i32]),
@@ -109,6 +112,23 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
         if len(t.shape) != len(shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
+def _need_rows(t: torch.Tensor, name: str, dtype, rows: int, min_cols: int, device=None):
+    """A 2-D tensor whose rows may be strided (a slice of a wider buffer) but
+    whose elements inside a row are contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] < min_cols:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected ({rows}, >= {min_cols})")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit stride inside a row")
 
 
 @dataclass
@@ -227,3 +247,57 @@ def sparse_mla_decode(batch: Batch, q, kv_cache, indices, softmax_scale, out, ls
                                    int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(dev))
     _check(st, "dsa_sparse_mla_decode")
     return out, lse
+
+
+def indexer_q_quant_fp8(q, weights, q_fp8=None, weights_out=None):
+    """dsa_indexer_q_quant_fp8: q [R, 64, 128] bf16 and weights [R, 64] fp32 ->
+    (q_fp8 [R, 64, 128] uint8 e4m3fn codes, weights_out [R, 64] fp32 with the
+    per-(row, head) scale folded in).  ``weights_out`` may be ``weights``."""
+    lib = load()
+    dev = q.device
+    R = int(q.shape[0])
+    _need(q, "q", torch.bfloat16, (R, IDX_HEADS, IDX_DIM), dev)
+    _need(weights, "weights", torch.float32, (R, IDX_HEADS), dev)
+    if q_fp8 is None:
+        q_fp8 = torch.empty(R, IDX_HEADS, IDX_DIM, dtype=torch.uint8, device=dev)
+    if weights_out is None:
+        weights_out = torch.empty(R, IDX_HEADS, dtype=torch.float32, device=dev)
+    _need(q_fp8, "q_fp8", torch.uint8, (R, IDX_HEADS, IDX_DIM), dev)
+    _need(weights_out, "weights_out", torch.float32, (R, IDX_HEADS), dev)
+    st = lib.dsa_indexer_q_quant_fp8(R, _ptr(q), _ptr(weights), _ptr(q_fp8), _ptr(weights_out), _stream(dev))
+    _check(st, "dsa_indexer_q_quant_fp8")
+    return q_fp8, weights_out
+
+
+def indexer_k_quant_and_cache(k, slot_mapping, idx_cache):
+    """dsa_indexer_k_quant_and_cache: quantise k [T, >=128] bf16 (rows may be
+    strided) and write it into idx_cache [num_pages, page_stride] uint8 at the
+    slots of slot_mapping [T] int64.  Returns idx_cache."""
+    lib = load()
+    dev = k.device
+    T = int(k.shape[0])
+    _need_rows(k, "k", torch.bfloat16, T, IDX_DIM, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+    _need(idx_cache, "idx_cache", torch.uint8, (None, None), dev)
+    st = lib.dsa_indexer_k_quant_and_cache(T, _ptr(k), int(k.stride(0)), _ptr(slot_mapping), _ptr(idx_cache),
+                                           int(idx_cache.shape[1]), int(idx_cache.shape[0]), _stream(dev))
+    _check(st, "dsa_indexer_k_quant_and_cache")
+    return idx_cache
+
+
+def latent_cache_write(latent, rope, slot_mapping, kv_cache):
+    """dsa_latent_cache_write: latent [T, >=512] and rope [T, >=64] bf16 (rows
+    may be strided) into kv_cache [num_pages, page_stride] bf16 at the slots of
+    slot_mapping [T] int64.  Returns kv_cache."""
+    lib = load()
+    dev = latent.device
+    T = int(latent.shape[0])
+    _need_rows(latent, "latent", torch.bfloat16, T, V_DIM, dev)
+    _need_rows(rope, "rope", torch.bfloat16, T, KV_DIM - V_DIM, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+    _need(kv_cache, "kv_cache", torch.bfloat16, (None, None), dev)
+    st = lib.dsa_latent_cache_write(T, _ptr(latent), int(latent.stride(0)), _ptr(rope), int(rope.stride(0)),
+                                    _ptr(slot_mapping), _ptr(kv_cache), int(kv_cache.shape[1]),
+                                    int(kv_cache.shape[0]), _stream(dev))
+    _check(st, "dsa_latent_cache_write")
+    return kv_cache

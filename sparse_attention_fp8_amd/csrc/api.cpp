@@ -18,6 +18,10 @@ namespace {
 // for it and depend on host fields only, so workspace queries need no GPU.
 constexpr int kTargetCUs = 256;
 
+// Largest row / token count one quantiser or cache-writer call takes (keeps
+// every grid far inside the 2^31 workgroup limit).
+constexpr int kMaxWriteItems = DSA_MAX_WRITE_ITEMS;
+
 thread_local std::string g_last_error;
 
 int fail(int status, const char* fmt, ...) {
@@ -217,6 +221,68 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
   return hip_status(dsa::launch_sparse_mla(to_args(batch), q, num_heads, kv_cache, kv_page_stride, indices, k,
                                            softmax_scale, p, out, lse, workspace, (hipStream_t)stream),
                     "dsa_sparse_mla_decode launch");
+}
+
+int dsa_indexer_q_quant_fp8(int32_t num_rows, const uint16_t* q, const float* weights, uint8_t* q_fp8,
+                            float* weights_out, void* stream) {
+  if (num_rows < 0 || num_rows > kMaxWriteItems)
+    return fail(DSA_ERR_UNSUPPORTED, "num_rows=%d outside [0, %d]", num_rows, kMaxWriteItems);
+  if (num_rows == 0) return ok();
+  if (!q || !weights || !q_fp8 || !weights_out)
+    return fail(DSA_ERR_NULL, "q, weights, q_fp8 and weights_out must not be NULL");
+  if (!aligned(q, 16)) return fail(DSA_ERR_INVALID, "q must be 16-byte aligned");
+  if (!aligned(q_fp8, 8)) return fail(DSA_ERR_INVALID, "q_fp8 must be 8-byte aligned");
+  if (!aligned(weights, 4) || !aligned(weights_out, 4))
+    return fail(DSA_ERR_INVALID, "weights and weights_out must be 4-byte aligned");
+  return hip_status(dsa::launch_indexer_q_quant(num_rows, q, weights, q_fp8, weights_out, (hipStream_t)stream),
+                    "dsa_indexer_q_quant_fp8 launch");
+}
+
+int dsa_indexer_k_quant_and_cache(int32_t num_tokens, const uint16_t* k, int64_t k_stride,
+                                  const int64_t* slot_mapping, uint8_t* idx_cache, int64_t idx_page_stride,
+                                  int32_t num_pages, void* stream) {
+  if (num_tokens < 0 || num_tokens > kMaxWriteItems)
+    return fail(DSA_ERR_UNSUPPORTED, "num_tokens=%d outside [0, %d]", num_tokens, kMaxWriteItems);
+  if (num_pages < 0) return fail(DSA_ERR_INVALID, "num_pages=%d < 0", num_pages);
+  if (k_stride < DSA_INDEXER_DIM || k_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID, "k_stride=%lld must be >= 128 elements and a multiple of 8", (long long)k_stride);
+  if (idx_page_stride < DSA_INDEXER_PAGE_BYTES || idx_page_stride % 16 != 0)
+    return fail(DSA_ERR_INVALID, "idx_page_stride=%lld must be >= 8448 bytes and a multiple of 16",
+                (long long)idx_page_stride);
+  if (num_tokens == 0 || num_pages == 0) return ok();
+  if (!k || !slot_mapping || !idx_cache) return fail(DSA_ERR_NULL, "k, slot_mapping and idx_cache must not be NULL");
+  if (!aligned(k, 16) || !aligned(idx_cache, 16))
+    return fail(DSA_ERR_INVALID, "k and idx_cache must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(DSA_ERR_INVALID, "slot_mapping must be 8-byte aligned");
+  return hip_status(dsa::launch_indexer_k_quant_cache(num_tokens, k, k_stride, slot_mapping, idx_cache,
+                                                      idx_page_stride, num_pages, (hipStream_t)stream),
+                    "dsa_indexer_k_quant_and_cache launch");
+}
+
+int dsa_latent_cache_write(int32_t num_tokens, const uint16_t* latent, int64_t latent_stride, const uint16_t* rope,
+                           int64_t rope_stride, const int64_t* slot_mapping, uint16_t* kv_cache,
+                           int64_t kv_page_stride, int32_t num_pages, void* stream) {
+  if (num_tokens < 0 || num_tokens > kMaxWriteItems)
+    return fail(DSA_ERR_UNSUPPORTED, "num_tokens=%d outside [0, %d]", num_tokens, kMaxWriteItems);
+  if (num_pages < 0) return fail(DSA_ERR_INVALID, "num_pages=%d < 0", num_pages);
+  if (latent_stride < DSA_V_DIM || latent_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID, "latent_stride=%lld must be >= 512 elements and a multiple of 8",
+                (long long)latent_stride);
+  if (rope_stride < DSA_KV_DIM - DSA_V_DIM || rope_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID, "rope_stride=%lld must be >= 64 elements and a multiple of 8", (long long)rope_stride);
+  if (kv_page_stride < (int64_t)DSA_PAGE_SIZE * DSA_KV_DIM || kv_page_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID, "kv_page_stride=%lld must be >= 36864 elements and a multiple of 8",
+                (long long)kv_page_stride);
+  if (num_tokens == 0 || num_pages == 0) return ok();
+  if (!latent || !rope || !slot_mapping || !kv_cache)
+    return fail(DSA_ERR_NULL, "latent, rope, slot_mapping and kv_cache must not be NULL");
+  if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(kv_cache, 16))
+    return fail(DSA_ERR_INVALID, "latent, rope and kv_cache must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(DSA_ERR_INVALID, "slot_mapping must be 8-byte aligned");
+  return hip_status(dsa::launch_latent_cache_write(num_tokens, latent, latent_stride, rope, rope_stride,
+                                                   slot_mapping, kv_cache, kv_page_stride, num_pages,
+                                                   (hipStream_t)stream),
+                    "dsa_latent_cache_write launch");
 }
 
 }  // extern "C"

@@ -37,4 +37,12 @@ hipError_t launch_sparse_mla(const BatchArgs& batch, const uint16_t* q, int H, c
                              const MlaPlan& plan, uint16_t* out, float* lse, void* workspace,
                              hipStream_t stream);
 
+hipError_t launch_indexer_q_quant(int num_rows, const uint16_t* q, const float* w, uint8_t* codes, float* w_out,
+                                  hipStream_t stream);
+hipError_t launch_indexer_k_quant_cache(int num_tokens, const uint16_t* k, int64_t k_stride, const int64_t* slots,
+                                        uint8_t* cache, int64_t page_stride, int num_pages, hipStream_t stream);
+hipError_t launch_latent_cache_write(int num_tokens, const uint16_t* latent, int64_t latent_stride,
+                                     const uint16_t* rope, int64_t rope_stride, const int64_t* slots,
+                                     uint16_t* cache, int64_t page_stride, int num_pages, hipStream_t stream);
+
 }  // namespace dsa

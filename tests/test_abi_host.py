@@ -40,7 +40,8 @@ def batch(**kw):
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"dsa_indexer_logits_paged", "dsa_indexer_logits_prefill", "dsa_topk",
-            "dsa_sparse_mla_decode"} <= set(names)
+            "dsa_sparse_mla_decode", "dsa_indexer_q_quant_fp8", "dsa_indexer_k_quant_and_cache",
+            "dsa_latent_cache_write"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -167,3 +168,59 @@ def test_binding_rejects_host_tensors():
                   num_pages=1)
     with pytest.raises(ValueError):
         b.c_struct()
+
+
+# --------------------------------------------------------------------------
+# quantiser and cache writers
+
+def test_q_quant_rejects_bad_arguments(lib):
+    f = lib.dsa_indexer_q_quant_fp8
+    assert f(0, None, None, None, None, None) == OK                  # nothing to do
+    assert f(-1, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUPPORTED
+    assert f((1 << 24) + 1, FAKE, FAKE, FAKE, FAKE, None) == ERR_UNSUPPORTED
+    assert f(4, FAKE, None, FAKE, FAKE, None) == ERR_NULL
+    assert f(4, FAKE + 8, FAKE, FAKE, FAKE, None) == ERR_INVALID      # q not 16-byte aligned
+    assert b"q must be 16-byte aligned" in lib.dsa_last_error_message()
+    assert f(4, FAKE, FAKE, FAKE + 4, FAKE, None) == ERR_INVALID      # codes not 8-byte aligned
+    assert f(4, FAKE, FAKE + 2, FAKE, FAKE, None) == ERR_INVALID
+
+
+def k_write(lib, **kw):
+    a = dict(T=10, k=FAKE, k_stride=128, slots=FAKE, cache=FAKE, stride=8448, pages=4)
+    a.update(kw)
+    return lib.dsa_indexer_k_quant_and_cache(a["T"], a["k"], a["k_stride"], a["slots"], a["cache"], a["stride"],
+                                             a["pages"], None)
+
+
+def test_k_writer_rejects_bad_arguments(lib):
+    assert k_write(lib, T=0, k=None, slots=None, cache=None) == OK
+    assert k_write(lib, pages=0, cache=None) == OK                    # no page to write
+    assert k_write(lib, T=-3) == ERR_UNSUPPORTED
+    assert k_write(lib, pages=-1) == ERR_INVALID
+    assert k_write(lib, k_stride=120) == ERR_INVALID
+    assert k_write(lib, k_stride=132) == ERR_INVALID                  # not a multiple of 8
+    assert k_write(lib, stride=8440) == ERR_INVALID
+    assert b"idx_page_stride" in lib.dsa_last_error_message()
+    assert k_write(lib, stride=8456) == ERR_INVALID                   # not a multiple of 16
+    assert k_write(lib, slots=None) == ERR_NULL
+    assert k_write(lib, k=FAKE + 8) == ERR_INVALID
+    assert k_write(lib, slots=FAKE + 4) == ERR_INVALID
+
+
+def latent_write(lib, **kw):
+    a = dict(T=10, lat=FAKE, lat_stride=512, rope=FAKE, rope_stride=64, slots=FAKE, cache=FAKE, stride=36864,
+             pages=4)
+    a.update(kw)
+    return lib.dsa_latent_cache_write(a["T"], a["lat"], a["lat_stride"], a["rope"], a["rope_stride"], a["slots"],
+                                      a["cache"], a["stride"], a["pages"], None)
+
+
+def test_latent_writer_rejects_bad_arguments(lib):
+    assert latent_write(lib, T=0, lat=None, rope=None, slots=None, cache=None) == OK
+    assert latent_write(lib, T=(1 << 24) + 1) == ERR_UNSUPPORTED
+    assert latent_write(lib, lat_stride=504) == ERR_INVALID
+    assert latent_write(lib, rope_stride=60) == ERR_INVALID
+    assert latent_write(lib, stride=36864 - 8) == ERR_INVALID
+    assert b"kv_page_stride" in lib.dsa_last_error_message()
+    assert latent_write(lib, rope=None) == ERR_NULL
+    assert latent_write(lib, cache=FAKE + 8) == ERR_INVALID
