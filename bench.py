@@ -132,6 +132,67 @@ def cpu_baseline(wl, budget_s):
                       f"{dt:.1f} s, scaled by {R}/{done}"}
 
 
+def pre_path(dsa, wl, batch_dev, base, dev, steps):
+    """Times the steps just before the path on this workload's new tokens: the
+    indexer-q quantiser over its R rows, and the indexer-K and latent cache
+    writers for the R tokens this step appends (the last q_len positions of
+    each sequence).  Inputs rotate through enough copies that one round moves
+    more than 1 GB, so the Infinity Cache cannot serve re-reads."""
+    R = wl.num_rows
+    if R == 0:
+        return {}
+    seq_lens = wl.seq_lens.numpy().astype(np.int64)
+    qs = wl.query_start.numpy().astype(np.int64)
+    bt = wl.block_table.numpy().astype(np.int64)
+    slots = np.empty(R, dtype=np.int64)
+    for b in range(len(seq_lens)):
+        ql = int(qs[b + 1] - qs[b])
+        pos = seq_lens[b] - ql + np.arange(ql)
+        slots[qs[b]:qs[b + 1]] = bt[b, pos // 64] * 64 + pos % 64
+    per = {"indexer_q_quant_fp8": R * 64 * (256 + 128 + 4 + 4),
+           "indexer_k_quant_and_cache": R * (256 + 128 + 4 + 8),
+           "latent_cache_write": R * (1152 + 1152 + 8)}
+    copies = int(min(16, max(2, math.ceil(1.0e9 / max(per["indexer_q_quant_fp8"], 1)))))
+    g = torch.Generator().manual_seed(1234)
+    ins = []
+    for _ in range(copies):
+        ins.append({"q": torch.randn(R, 64, 128, generator=g).to(torch.bfloat16).to(dev),
+                    "w": (torch.randn(R, 64, generator=g) / 8).to(dev),
+                    "k": torch.randn(R, 128, generator=g).to(torch.bfloat16).to(dev),
+                    "lat": torch.randn(R, 512, generator=g).to(torch.bfloat16).to(dev),
+                    "rope": torch.randn(R, 64, generator=g).to(torch.bfloat16).to(dev)})
+    slot_t = torch.from_numpy(slots).to(dev)
+    q8 = torch.empty(R, 64, 128, dtype=torch.uint8, device=dev)
+    w2 = torch.empty(R, 64, dtype=torch.float32, device=dev)
+    ops = {
+        "indexer_q_quant_fp8": lambda x: dsa.indexer_q_quant_fp8(x["q"], x["w"], q8, w2),
+        "indexer_k_quant_and_cache": lambda x: dsa.indexer_k_quant_and_cache(x["k"], slot_t, base["idx_cache"]),
+        "latent_cache_write": lambda x: dsa.latent_cache_write(x["lat"], x["rope"], slot_t, base["kv_cache"]),
+    }
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, fn in ops.items():
+        for x in ins:
+            fn(x)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for x in ins:
+                fn(x)
+        graph.replay()
+        rounds = max(2, steps // copies)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(rounds):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (rounds * copies)
+        gbs = per[name] / (us * 1e-6) / 1e9
+        res[name] = {"us": us, "bytes": per[name], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                     "items": R}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -282,6 +343,7 @@ def main():
                   f"{reps} launches of one entry point",
         "rows_per_s": R * 1000.0 / ms,
     }
+    line["pre_path"] = pre_path(dsa, wl, batch, base, dev, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
