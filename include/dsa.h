@@ -30,6 +30,13 @@
  *    query rows to num_rows, block-table entries outside [0, num_pages) mark
  *    their tokens masked, and top-k indices outside a row's causal range are
  *    masked, never dereferenced.
+ *  - Determinism: the same inputs give bit-identical outputs on every call
+ *    (fixed reduction orders; the only atomics count integers).  Batch
+ *    invariance: a row's logits over [0, e_r) and its top-k indices depend on
+ *    that row's own inputs only; so do its sparse MLA out and lse when
+ *    num_splits = 1.  The automatic split count follows the batch shape, which
+ *    changes the summation order of the split merge (the pages' backend
+ *    forces one split for batch-invariant runs: PR page, Limitations).
  *
  * Geometry of a step
  * ------------------
@@ -166,7 +173,8 @@ int dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_strid
  *  kv_cache    latent pages, 16-byte aligned; kv_page_stride in elements
  *  indices     [R, k] int32 logical token ids (typically dsa_topk's output)
  *  k           1 <= k <= DSA_MAX_TOPK
- *  num_splits  0 = automatic (dsa_sparse_mla_pick_splits), 1 = single pass,
+ *  num_splits  0 = automatic (dsa_sparse_mla_pick_splits), 1 = single pass
+ *              (batch-invariant: a row's results do not depend on the batch),
  *              n > 1 = the k slots cut into n contiguous ranges merged N-way
  *              (clamped to the number of 64-slot tiles)
  *  out         [R, H, 512] bf16;  lse [R, H] fp32 (either may not be NULL)
