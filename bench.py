@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "x1m"])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate through (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -333,7 +333,8 @@ def main():
         "dtype": "fp8 indexer / bf16 MLA, fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": synth.CONFIGS[args.config], "name": args.config, "rows": R, "mla_heads": H,
-                   "topk": k, "splits": splits, "cache_copies": copies, "seed": args.seed or int(args.config[1:])},
+                   "topk": k, "splits": splits, "cache_copies": copies,
+                   "seed": args.seed if args.seed is not None else synth.DEFAULT_SEEDS[args.config]},
         "roofline": roof,
         "stages_ms": stage_ms,
         "step_bytes": total_bytes,

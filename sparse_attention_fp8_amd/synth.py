@@ -205,7 +205,11 @@ CONFIGS = {
     "c3": "long-context decode, batch 1, context 131072, 16 MLA heads",
     "c4": "chunked prefill, 4096 queries appended to a 61440-token prefix, 16 MLA heads",
     "c5": "MTP decode, batch 64, 2 queries per sequence, contexts log-uniform in [1024, 65536], 128 MLA heads",
+    # beyond the five: the longest row one top-k call takes (32 chunks of 32768 keys merged)
+    "x1m": "long-context decode, batch 1, context 1048576, 16 MLA heads",
 }
+
+DEFAULT_SEEDS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "x1m": 6}
 
 
 def config_shape(name: str, seed: int):
@@ -223,10 +227,12 @@ def config_shape(name: str, seed: int):
         lo, hi = math.log(1024.0), math.log(65536.0)
         L = np.floor(np.exp(rng.uniform(lo, hi, size=64))).astype(np.int64)
         return np.clip(L, 1024, 65536).tolist(), [2] * 64, 128
+    if name == "x1m":
+        return [1 << 20], [1], 16
     raise KeyError(name)
 
 
 def make_config(name: str, seed: int | None = None, **kw) -> Workload:
-    seed = int(name[1:]) if seed is None else seed
+    seed = DEFAULT_SEEDS[name] if seed is None else seed
     seq_lens, q_lens, heads = config_shape(name, seed)
     return make_workload(seq_lens, q_lens, heads, seed, name=name, **kw)

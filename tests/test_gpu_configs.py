@@ -1,4 +1,6 @@
-"""Full-size workloads c1..c5 in the launch configuration bench.py times.
+"""Full-size workloads c1..c5 (and x1m, one 1,048,576-token decode row: the
+longest row one top-k call takes, 32 chunks merged) in the launch
+configuration bench.py times.
 
 Each test runs one whole step on the GPU (indexer -- the prefill entry for the
 chunked-prefill workload --, top-k with its workspace, sparse MLA with the
@@ -48,7 +50,7 @@ def run_step(dsa, wl):
     return stride, logits, indices, out, lse
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5", "x1m"])
 def test_config_sampled_rows(dsa, name):
     wl = synth.make_config(name)
     stride, logits, indices, out, lse = run_step(dsa, wl)
