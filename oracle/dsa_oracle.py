@@ -38,6 +38,10 @@ What it computes, and where each step comes from:
   their arithmetic (one amax / 448 scale per 128 values, round-to-nearest-even
   saturating e4m3fn codes, decided in fp32) is stated where they are written
   out, with the bf16 latent-cache writer beside them.
+* FP8 latent cache.  The PR page (Limitations) names the bf16-only latent cache
+  as a gap; the fp8 layout read here (4 scale groups of 128 latent values,
+  bf16 rope) is defined where it is written out (``latent_cache_write_fp8``)
+  and sparse MLA over it attends over the dequantised rows.
 """
 from __future__ import annotations
 
@@ -189,12 +193,13 @@ def topk(logits, seq_lens, query_start, k, rows=None):
 # --------------------------------------------------------------------------
 # sparse MLA
 
-def _selected_rows(kv_cache, bt_row, idx_list, e, num_pages):
+def _selected_rows(kv_cache, bt_row, idx_list, e, num_pages, kv_format="bf16"):
     """Latent rows [n, 576] (float64) of the valid entries of an index list.
 
     Valid entries are 0 <= s < e whose block maps to a page in [0, num_pages);
     everything else (the -1 padding included) is masked and never read.
-    Duplicates are kept, in list order.
+    Duplicates are kept, in list order.  ``kv_format`` "fp8" reads the fp8
+    latent cache (dequantised rows, see ``kv8_rows``).
     """
     kv = np.asarray(kv_cache)
     s = np.asarray(idx_list, dtype=np.int64)
@@ -204,19 +209,22 @@ def _selected_rows(kv_cache, bt_row, idx_list, e, num_pages):
     page, slot = token_location(bt_row, s)
     ok = (page >= 0) & (page < num_pages)
     page, slot = page[ok], slot[ok]
+    if kv_format == "fp8":
+        return kv8_rows(kv, page, slot) if page.size else np.zeros((0, KV_DIM))
     cols = slot[:, None] * KV_DIM + np.arange(KV_DIM)[None, :]
     return bf16_decode(kv[page[:, None], cols])
 
 
 def sparse_mla(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
-               softmax_scale, num_pages=None, rows=None):
+               softmax_scale, num_pages=None, rows=None, kv_format="bf16"):
     """Single-pass sparse MLA: (out [R, H, 512] float64, lse [R, H] float64).
 
     For each row and head over the row's valid selected latent rows c_j:
     z_j = scale * q . c_j (576 dims); out = sum softmax(z)_j c_j[:512];
     lse = ln sum_j exp(z_j).  A row with no valid entry gives out = 0 and
     lse = -inf.  With ``rows``, ``indices`` and the outputs hold just those
-    rows, in that order.
+    rows, in that order.  ``kv_format`` "fp8": the cache is the fp8 latent
+    cache and c_j its dequantised rows.
     """
     q_u16 = np.asarray(q_mla)
     R, H, _ = q_u16.shape
@@ -228,7 +236,7 @@ def sparse_mla(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
     out = np.zeros((len(row_list), H, V_DIM))
     lse = np.full((len(row_list), H), -np.inf)
     for o, r in enumerate(row_list):
-        C = _selected_rows(kv_cache, bt[seq[r]], indices[o], int(ext[r]), num_pages)
+        C = _selected_rows(kv_cache, bt[seq[r]], indices[o], int(ext[r]), num_pages, kv_format)
         if C.shape[0] == 0:
             continue
         Q = bf16_decode(q_u16[r])                       # [H, 576]
@@ -242,7 +250,7 @@ def sparse_mla(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
 
 
 def sparse_mla_split(q_mla, kv_cache, block_table, seq_lens, query_start, indices,
-                     softmax_scale, num_splits, num_pages=None, rows=None):
+                     softmax_scale, num_splits, num_pages=None, rows=None, kv_format="bf16"):
     """Split-KV sparse MLA with the N-way online-softmax merge.
 
     The k slots of each row's index list are cut into ``num_splits`` contiguous
@@ -270,7 +278,7 @@ def sparse_mla_split(q_mla, kv_cache, block_table, seq_lens, query_start, indice
         ms, ls, accs = [], [], []
         for i in range(num_splits):
             C = _selected_rows(kv_cache, bt[seq[r]], idx[o, i * per:(i + 1) * per],
-                               int(ext[r]), num_pages)
+                               int(ext[r]), num_pages, kv_format)
             m = np.full(H, MASK_SENTINEL)
             l = np.zeros(H)
             acc = np.zeros((H, V_DIM))
@@ -382,3 +390,51 @@ def latent_cache_write(latent_bf16, rope_bf16, slot_mapping, kv_cache):
         cache[p, s * KV_DIM:s * KV_DIM + V_DIM] = lat[i]
         cache[p, s * KV_DIM + V_DIM:(s + 1) * KV_DIM] = rope[i]
     return cache
+
+
+# --------------------------------------------------------------------------
+# fp8 latent cache (the pages list the bf16-only latent cache as a limitation
+# of their backend, PR page "Limitations"; they define no fp8 layout)
+#
+# Reading taken: the 512 latent values of a token are quantised in 4 groups of
+# 128 with the same quantiser as the indexer (amax / 448 fp32 scale, RNE
+# saturating e4m3fn); the 64 rope values stay bf16.  Page of 64 tokens: row
+# t at byte 640 t holds the 512 codes then the 64 bf16 rope values (640 B);
+# the 4 fp32 scales of token t sit at byte 40960 + 16 t.  A token's latent
+# value d is scale[d // 128] * e4m3(code[d]).
+
+KV8_ROW_BYTES = 640
+KV8_SCALE_OFFSET = PAGE * KV8_ROW_BYTES           # 40960
+KV8_PAGE_BYTES = KV8_SCALE_OFFSET + PAGE * 16     # 41984
+
+
+def latent_cache_write_fp8(latent_bf16, rope_bf16, slot_mapping, kv8_cache):
+    """Quantise each token's latent [512] (4 groups of 128) and write codes,
+    rope bits and scales into a copy of the fp8 latent cache
+    [num_pages, page_stride] uint8."""
+    cache = np.array(kv8_cache, dtype=np.uint8, copy=True)
+    lat = np.asarray(latent_bf16).reshape(-1, 4, 128)
+    codes, scale = quantize_groups_fp8(lat)                 # [T, 4, 128], [T, 4]
+    rope = np.ascontiguousarray(np.asarray(rope_bf16, dtype=np.uint16))
+    t, page, slot = _slot_targets(slot_mapping, cache.shape[0])
+    for i, p, s in zip(t, page, slot):
+        row = s * KV8_ROW_BYTES
+        cache[p, row:row + V_DIM] = codes[i].reshape(-1)
+        cache[p, row + V_DIM:row + KV8_ROW_BYTES] = rope[i].view(np.uint8)
+        cache[p, KV8_SCALE_OFFSET + 16 * s:KV8_SCALE_OFFSET + 16 * s + 16] = \
+            np.ascontiguousarray(scale[i].astype(np.float32)).view(np.uint8)
+    return cache
+
+
+def kv8_rows(kv8_cache, page, slot):
+    """Dequantised latent rows [n, 576] (float64) of (page, slot) pairs."""
+    cache = np.asarray(kv8_cache, dtype=np.uint8)
+    page = np.asarray(page, dtype=np.int64)
+    slot = np.asarray(slot, dtype=np.int64)
+    cols = slot[:, None] * KV8_ROW_BYTES + np.arange(KV8_ROW_BYTES)[None, :]
+    raw = cache[page[:, None], cols]                                  # [n, 640]
+    sc_cols = KV8_SCALE_OFFSET + 16 * slot[:, None] + np.arange(16)[None, :]
+    scale = np.ascontiguousarray(cache[page[:, None], sc_cols]).view(np.float32).astype(np.float64)  # [n, 4]
+    lat = e4m3fn_decode(raw[:, :V_DIM]).reshape(-1, 4, 128) * scale[:, :, None]
+    rope = bf16_decode(np.ascontiguousarray(raw[:, V_DIM:]).view(np.uint16))
+    return np.concatenate([lat.reshape(-1, V_DIM), rope], axis=1)

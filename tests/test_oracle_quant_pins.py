@@ -211,3 +211,74 @@ def test_latent_writer_matches_explicit_layout():
             one = build_kv_cache(row[None], [0], 1, stride)
             want[s // 64, (s % 64) * 576:(s % 64 + 1) * 576] = one[0, :576]
     assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------------------
+# fp8 latent cache
+
+def test_fp8_latent_writer_matches_explicit_layout_and_round_trips():
+    rng = np.random.default_rng(11)
+    num_pages, T, stride = 3, 70, oracle.KV8_PAGE_BYTES + 64
+    cache0 = rng.integers(0, 256, (num_pages, stride), dtype=np.uint8)
+    lat_f = rng.standard_normal((T, 512)) * np.exp2(rng.integers(-4, 5, (T, 4))).repeat(128, axis=1)
+    lat = to_bf16_bits(lat_f)
+    rope = to_bf16_bits(rng.standard_normal((T, 64)))
+    slots = slot_case(num_pages, T, rng)
+    got = oracle.latent_cache_write_fp8(lat, rope, slots, cache0)
+    want = cache0.copy()
+    for t in range(T):
+        s = int(slots[t])
+        if not 0 <= s < num_pages * 64:
+            continue
+        p, sl = s // 64, s % 64
+        for g in range(4):
+            codes, scale = oracle.quantize_groups_fp8(lat[t, 128 * g:128 * (g + 1)][None])
+            want[p, sl * 640 + 128 * g:sl * 640 + 128 * (g + 1)] = codes[0]
+            want[p, 40960 + 16 * sl + 4 * g:40960 + 16 * sl + 4 * g + 4] = np.float32(scale[0]).reshape(1).view(np.uint8)
+        want[p, sl * 640 + 512:sl * 640 + 640] = rope[t].view(np.uint8)
+    assert np.array_equal(got, want)
+    ok = (slots >= 0) & (slots < num_pages * 64)
+    rows = oracle.kv8_rows(got, slots[ok] // 64, slots[ok] % 64)
+    x = oracle.bf16_decode(lat[ok])
+    sc = np.abs(x).reshape(-1, 4, 128).max(axis=2).repeat(128, axis=1) / 448
+    assert (np.abs(rows[:, :512] - x) <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sc) * 1.0001).all()
+    assert np.array_equal(rows[:, 512:], oracle.bf16_decode(rope[ok]))
+
+
+def exact_fp8_latent(rng, T):
+    """Latent rows whose every group is an e4m3 value times a power of two, with
+    one element on the top code: the quantiser reproduces them exactly."""
+    codes = rng.integers(0, 0x7F, (T, 4, 128)).astype(np.uint8) | (rng.integers(0, 2, (T, 4, 128)) << 7).astype(np.uint8)
+    codes[:, :, 0] = 0x7E
+    e = rng.integers(-8, 4, (T, 4, 1))
+    return (oracle.e4m3fn_decode(codes) * np.exp2(e)).reshape(T, 512)
+
+
+def test_fp8_cache_mla_equals_bf16_cache_mla_on_exactly_representable_rows():
+    """Rows the fp8 format holds exactly (and bf16 too): sparse MLA over the fp8
+    cache must equal sparse MLA over a bf16 cache of the same values."""
+    rng = np.random.default_rng(12)
+    seq_lens, q_lens, H = [300, 2200], [1, 2], 16
+    wl = synth.make_workload(seq_lens, q_lens, H, seed=3, spare_pages=2)
+    L = sum(seq_lens)
+    lat = exact_fp8_latent(rng, L)
+    rope = rng.standard_normal((L, 64))
+    bt = wl.block_table.numpy()
+    slots = np.concatenate([bt[b, np.arange(n) // 64].astype(np.int64) * 64 + np.arange(n) % 64
+                            for b, n in enumerate(seq_lens)])
+    kv8 = oracle.latent_cache_write_fp8(to_bf16_bits(lat), to_bf16_bits(rope), slots,
+                                        np.zeros((wl.num_pages, oracle.KV8_PAGE_BYTES), np.uint8))
+    kv16 = oracle.latent_cache_write(to_bf16_bits(lat), to_bf16_bits(rope), slots,
+                                     np.zeros((wl.num_pages, 64 * 576), np.uint16))
+    assert np.array_equal(oracle.kv8_rows(kv8, slots // 64, slots % 64),
+                          oracle.bf16_decode(kv16.reshape(-1, 576)[slots // 64 * 64 + slots % 64]))
+    idx = np.stack([np.sort(rng.choice(int(e), size=min(2048, int(e)), replace=False).tolist() +
+                            [-1] * (2048 - min(2048, int(e)))) for e in wl.row_extents()])
+    idx = np.where(idx < 0, -1, idx)
+    q = wl.q_mla.view(torch.int16).numpy()
+    args = (bt, wl.seq_lens.numpy(), wl.query_start.numpy(), idx, wl.softmax_scale)
+    o8, l8 = oracle.sparse_mla(q, kv8, *args, kv_format="fp8")
+    o16, l16 = oracle.sparse_mla(q, kv16, *args)
+    assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
+    o8s, l8s = oracle.sparse_mla_split(q, kv8, *args, 5, kv_format="fp8")
+    assert np.allclose(o8s, o8, atol=1e-12) and np.allclose(l8s, l8, atol=1e-12)
