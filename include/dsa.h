@@ -89,6 +89,7 @@ typedef enum {
 #define DSA_V_DIM 512
 #define DSA_MAX_TOPK 2048
 #define DSA_MAX_SEQS 4096
+#define DSA_KV8_PAGE_BYTES 41984      /* fp8 latent page: 64 x 640 B rows + 64 x 16 B scale records */
 #define DSA_MAX_WRITE_ITEMS (1 << 24) /* rows / tokens per quantiser or cache-writer call */
 
 /* One step's batch description, shared by all four calls. */
@@ -187,6 +188,28 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_sparse_mla_decode_fp8 -- dsa_sparse_mla_decode over an fp8 latent cache,
+ * which the pages list as missing from their backend (PR page, Limitations:
+ * bf16-only latent cache).  fp8 latent page (64 tokens, DSA_KV8_PAGE_BYTES):
+ *   bytes [640 t, 640 t + 512)        512 e4m3fn codes of token t's latent
+ *   bytes [640 t + 512, 640 t + 640)  its 64 rope values, bf16
+ *   bytes [40960 + 16 t, +16)         4 fp32 scales, one per 128 latent values
+ * Latent value d of token t = scale[d / 128] * e4m3(code[d]) (written by
+ * dsa_latent_cache_write_fp8).  The attention is computed over these
+ * dequantised rows exactly as dsa_sparse_mla_decode does over bf16 rows (q
+ * stays bf16; products are exact, sums fp32; the probabilities times the group
+ * scale are rounded to bf16 for the PV products).  Same arguments, masking,
+ * splits, workspace (dsa_sparse_mla_workspace_bytes) and outputs, except:
+ *  kv_cache_fp8          fp8 latent pages, 16-byte aligned
+ *  kv_page_stride_bytes  >= DSA_KV8_PAGE_BYTES, a multiple of 16 (128 keeps
+ *                        every row on whole 128-byte lines)
+ */
+int dsa_sparse_mla_decode_fp8(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads,
+                              const uint8_t* kv_cache_fp8, int64_t kv_page_stride_bytes, const int32_t* indices,
+                              int32_t k, float softmax_scale, int32_t num_splits, uint16_t* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The steps just before the path: the indexer-q quantiser and the two cache
  * writers (vllm-dsa-mtp-sm80 README, skew fixes 0 and 1, which name the
  * unfused per_token_group_quant_fp8 for the indexer q and the indexer-K cache
@@ -250,6 +273,19 @@ int dsa_indexer_k_quant_and_cache(int32_t num_tokens, const uint16_t* k, int64_t
 int dsa_latent_cache_write(int32_t num_tokens, const uint16_t* latent, int64_t latent_stride, const uint16_t* rope,
                            int64_t rope_stride, const int64_t* slot_mapping, uint16_t* kv_cache,
                            int64_t kv_page_stride, int32_t num_pages, void* stream);
+
+/*
+ * dsa_latent_cache_write_fp8 -- quantise each new token's latent row in 4
+ * groups of 128 (the quantiser above) and write codes, scales and the bf16 rope
+ * part into its slot of the fp8 latent cache (layout at
+ * dsa_sparse_mla_decode_fp8).  Arguments as dsa_latent_cache_write, with
+ *  kv_cache_fp8          fp8 latent pages, 16-byte aligned
+ *  kv_page_stride_bytes  >= DSA_KV8_PAGE_BYTES, a multiple of 16
+ */
+int dsa_latent_cache_write_fp8(int32_t num_tokens, const uint16_t* latent, int64_t latent_stride,
+                               const uint16_t* rope, int64_t rope_stride, const int64_t* slot_mapping,
+                               uint8_t* kv_cache_fp8, int64_t kv_page_stride_bytes, int32_t num_pages,
+                               void* stream);
 
 /* Workspace sizes (host fields of `batch` only; 0 when none is needed). */
 size_t dsa_topk_workspace_bytes(const dsa_batch_t* batch, int32_t k);

@@ -7,5 +7,6 @@ marshalling through ctypes) plus the synthetic-workload generator.
 from .binding import (  # noqa: F401
     DSAError, load, library_path, indexer_logits_paged, indexer_logits_prefill, topk,
     sparse_mla_decode, topk_workspace_bytes, sparse_mla_workspace_bytes, sparse_mla_pick_splits,
-    indexer_q_quant_fp8, indexer_k_quant_and_cache, latent_cache_write, Batch,
+    indexer_q_quant_fp8, indexer_k_quant_and_cache, latent_cache_write, sparse_mla_decode_fp8,
+    latent_cache_write_fp8, Batch,
 )

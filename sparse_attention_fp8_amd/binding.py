@@ -24,6 +24,7 @@ IDX_PAGE_BYTES = 8448
 KV_DIM = 576
 V_DIM = 512
 MAX_TOPK = 2048
+KV8_PAGE_BYTES = 41984    # fp8 latent page: 64 x (512 e4m3 + 64 bf16) rows, then 64 x 4 fp32 scales
 
 
 class DSAError(RuntimeError):
@@ -63,6 +64,8 @@ def load():
         "dsa_indexer_logits_prefill": (ctypes.c_int, [B, vp, vp, vp, i64, vp, i64, ctypes.c_int, vp]),
         "dsa_topk": (ctypes.c_int, [B, vp, i64, i32, vp, vp, sz, vp]),
         "dsa_sparse_mla_decode": (ctypes.c_int, [B, vp, i32, vp, i64, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
+        "dsa_sparse_mla_decode_fp8": (ctypes.c_int, [B, vp, i32, vp, i64, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
+        "dsa_latent_cache_write_fp8": (ctypes.c_int, [i32, vp, i64, vp, i64, vp, vp, i64, i32, vp]),
         "dsa_indexer_q_quant_fp8": (ctypes.c_int, [i32, vp, vp, vp, vp, vp]),
         "dsa_indexer_k_quant_and_cache": (ctypes.c_int, [i32, vp, i64, vp, vp, i64, i32, vp]),
         "dsa_latent_cache_write": (ctypes.c_int, [i32, vp, i64, vp, i64, vp, vp, i64, i32, vp]),
@@ -301,3 +304,46 @@ def latent_cache_write(latent, rope, slot_mapping, kv_cache):
                                     int(kv_cache.shape[0]), _stream(dev))
     _check(st, "dsa_latent_cache_write")
     return kv_cache
+
+
+def sparse_mla_decode_fp8(batch: Batch, q, kv_cache_fp8, indices, softmax_scale, out, lse, num_splits=0,
+                          workspace=None):
+    """dsa_sparse_mla_decode_fp8 over an fp8 latent cache [num_pages, page_stride_bytes] uint8 into ``out``
+    [R, H, 512] bf16 and ``lse`` [R, H] fp32 (returned)."""
+    lib = load()
+    dev = batch.device
+    R = batch.num_rows
+    _need(q, "q", torch.bfloat16, (R, None, KV_DIM), dev)
+    H = int(q.shape[1])
+    _need(kv_cache_fp8, "kv_cache_fp8", torch.uint8, (batch.num_pages, None), dev)
+    _need(indices, "indices", torch.int32, (R, None), dev)
+    k = int(indices.shape[1])
+    _need(out, "out", torch.bfloat16, (R, H, V_DIM), dev)
+    _need(lse, "lse", torch.float32, (R, H), dev)
+    need = sparse_mla_workspace_bytes(batch, H, k, num_splits)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.dsa_sparse_mla_decode_fp8(ctypes.byref(batch.c_struct()), _ptr(q), H, _ptr(kv_cache_fp8),
+                                       int(kv_cache_fp8.shape[1]), _ptr(indices), k, float(softmax_scale),
+                                       int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(dev))
+    _check(st, "dsa_sparse_mla_decode_fp8")
+    return out, lse
+
+
+def latent_cache_write_fp8(latent, rope, slot_mapping, kv_cache_fp8):
+    """dsa_latent_cache_write_fp8: quantise latent [T, >=512] (4 groups of 128) and copy rope [T, >=64]
+    (bf16, rows may be strided) into kv_cache_fp8 [num_pages, page_stride_bytes] uint8 at the slots of
+    slot_mapping [T] int64.  Returns kv_cache_fp8."""
+    lib = load()
+    dev = latent.device
+    T = int(latent.shape[0])
+    _need_rows(latent, "latent", torch.bfloat16, T, V_DIM, dev)
+    _need_rows(rope, "rope", torch.bfloat16, T, KV_DIM - V_DIM, dev)
+    _need(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+    _need(kv_cache_fp8, "kv_cache_fp8", torch.uint8, (None, None), dev)
+    st = lib.dsa_latent_cache_write_fp8(T, _ptr(latent), int(latent.stride(0)), _ptr(rope), int(rope.stride(0)),
+                                        _ptr(slot_mapping), _ptr(kv_cache_fp8), int(kv_cache_fp8.shape[1]),
+                                        int(kv_cache_fp8.shape[0]), _stream(dev))
+    _check(st, "dsa_latent_cache_write_fp8")
+    return kv_cache_fp8

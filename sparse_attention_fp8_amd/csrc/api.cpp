@@ -223,6 +223,69 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
                     "dsa_sparse_mla_decode launch");
 }
 
+int dsa_sparse_mla_decode_fp8(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads,
+                              const uint8_t* kv_cache_fp8, int64_t kv_page_stride_bytes, const int32_t* indices,
+                              int32_t k, float softmax_scale, int32_t num_splits, uint16_t* out, float* lse,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  if (!heads_supported(num_heads))
+    return fail(DSA_ERR_UNSUPPORTED, "num_heads=%d: supported are 16, 32 and multiples of 64 up to 1024", num_heads);
+  if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k=%d outside [1, %d]", k, DSA_MAX_TOPK);
+  if (kv_page_stride_bytes < DSA_KV8_PAGE_BYTES || kv_page_stride_bytes % 16 != 0)
+    return fail(DSA_ERR_INVALID, "kv_page_stride_bytes=%lld must be >= %d and a multiple of 16",
+                (long long)kv_page_stride_bytes, DSA_KV8_PAGE_BYTES);
+  if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID, "softmax_scale is not finite");
+  if (num_splits < 0) return fail(DSA_ERR_INVALID, "num_splits=%d < 0", num_splits);
+  if (batch->num_rows == 0) return ok();
+  if (!q || !indices || !out || !lse) return fail(DSA_ERR_NULL, "q, indices, out and lse must not be NULL");
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(DSA_ERR_INVALID, "q and out must be 16-byte aligned");
+  if (!aligned(indices, 4) || !aligned(lse, 4)) return fail(DSA_ERR_INVALID, "indices and lse must be 4-byte aligned");
+  if (batch->max_seq_len > 0 && batch->num_pages > 0) {
+    if (!kv_cache_fp8) return fail(DSA_ERR_NULL, "kv_cache_fp8 is NULL");
+    if (!aligned(kv_cache_fp8, 16)) return fail(DSA_ERR_INVALID, "kv_cache_fp8 must be 16-byte aligned");
+  }
+  const dsa::MlaPlan p = dsa::plan_sparse_mla(batch->num_rows, batch->max_seq_len, num_heads, k, num_splits, kTargetCUs);
+  const size_t need = dsa::sparse_mla_workspace_bytes(batch->num_rows, num_heads, p);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(DSA_ERR_WORKSPACE, "dsa_sparse_mla_decode_fp8 needs %zu workspace bytes, got %zu", need,
+                  workspace ? workspace_bytes : 0);
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
+  return hip_status(dsa::launch_sparse_mla_fp8(to_args(batch), q, num_heads, kv_cache_fp8, kv_page_stride_bytes,
+                                               indices, k, softmax_scale, p, out, lse, workspace,
+                                               (hipStream_t)stream),
+                    "dsa_sparse_mla_decode_fp8 launch");
+}
+
+int dsa_latent_cache_write_fp8(int32_t num_tokens, const uint16_t* latent, int64_t latent_stride,
+                               const uint16_t* rope, int64_t rope_stride, const int64_t* slot_mapping,
+                               uint8_t* kv_cache_fp8, int64_t kv_page_stride_bytes, int32_t num_pages,
+                               void* stream) {
+  if (num_tokens < 0 || num_tokens > kMaxWriteItems)
+    return fail(DSA_ERR_UNSUPPORTED, "num_tokens=%d outside [0, %d]", num_tokens, kMaxWriteItems);
+  if (num_pages < 0) return fail(DSA_ERR_INVALID, "num_pages=%d < 0", num_pages);
+  if (latent_stride < DSA_V_DIM || latent_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID, "latent_stride=%lld must be >= 512 elements and a multiple of 8",
+                (long long)latent_stride);
+  if (rope_stride < DSA_KV_DIM - DSA_V_DIM || rope_stride % 8 != 0)
+    return fail(DSA_ERR_INVALID, "rope_stride=%lld must be >= 64 elements and a multiple of 8", (long long)rope_stride);
+  if (kv_page_stride_bytes < DSA_KV8_PAGE_BYTES || kv_page_stride_bytes % 16 != 0)
+    return fail(DSA_ERR_INVALID, "kv_page_stride_bytes=%lld must be >= %d and a multiple of 16",
+                (long long)kv_page_stride_bytes, DSA_KV8_PAGE_BYTES);
+  if (num_tokens == 0 || num_pages == 0) return ok();
+  if (!latent || !rope || !slot_mapping || !kv_cache_fp8)
+    return fail(DSA_ERR_NULL, "latent, rope, slot_mapping and kv_cache_fp8 must not be NULL");
+  if (!aligned(latent, 16) || !aligned(rope, 16) || !aligned(kv_cache_fp8, 16))
+    return fail(DSA_ERR_INVALID, "latent, rope and kv_cache_fp8 must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(DSA_ERR_INVALID, "slot_mapping must be 8-byte aligned");
+  return hip_status(dsa::launch_latent_cache_write_fp8(num_tokens, latent, latent_stride, rope, rope_stride,
+                                                       slot_mapping, kv_cache_fp8, kv_page_stride_bytes, num_pages,
+                                                       (hipStream_t)stream),
+                    "dsa_latent_cache_write_fp8 launch");
+}
+
 int dsa_indexer_q_quant_fp8(int32_t num_rows, const uint16_t* q, const float* weights, uint8_t* q_fp8,
                             float* weights_out, void* stream) {
   if (num_rows < 0 || num_rows > kMaxWriteItems)

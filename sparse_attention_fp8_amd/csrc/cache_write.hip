@@ -143,7 +143,49 @@ __global__ __launch_bounds__(256) void latent_cache_write_kernel(const uint16_t*
   *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
 }
 
+// fp8 latent cache page: row t at 640 t = 512 e4m3 codes + 64 bf16 rope;
+// scale record (4 fp32) of token t at 40960 + 16 t.
+constexpr int kRow8 = 640;
+constexpr int kScaleOff8 = kPage * kRow8;
+
+// One wave per token: lanes 16 c .. 16 c + 15 quantise latent group c (dims
+// 128 c .. 128 c + 127), lanes 0..7 also copy 16 bytes of rope each.
+__global__ __launch_bounds__(256) void latent_cache_write_fp8_kernel(const uint16_t* __restrict__ latent,
+                                                                     int64_t latent_stride,
+                                                                     const uint16_t* __restrict__ rope,
+                                                                     int64_t rope_stride,
+                                                                     const int64_t* __restrict__ slots,
+                                                                     uint8_t* __restrict__ cache,
+                                                                     int64_t page_stride, int num_pages,
+                                                                     int num_tokens) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= num_tokens) return;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= (int64_t)num_pages * kPage) return;
+  const int c = lane >> 4, part = lane & 15;
+  const GroupValues vals = load_group_part(latent + (int64_t)t * latent_stride + c * kGroup + part * 8);
+  float scale;
+  const uint2 codes = quantise_part(vals, scale);
+  uint8_t* page = cache + (slot / kPage) * page_stride;
+  const int s = (int)(slot % kPage);
+  *reinterpret_cast<uint2*>(page + s * kRow8 + c * kGroup + part * 8) = codes;
+  if (part == 0) *reinterpret_cast<float*>(page + kScaleOff8 + 16 * s + 4 * c) = scale;
+  if (lane < 8)
+    *reinterpret_cast<uint4*>(page + s * kRow8 + kVDim + 16 * lane) =
+        *reinterpret_cast<const uint4*>(rope + (int64_t)t * rope_stride + 8 * lane);
+}
+
 }  // namespace
+
+hipError_t launch_latent_cache_write_fp8(int num_tokens, const uint16_t* latent, int64_t latent_stride,
+                                         const uint16_t* rope, int64_t rope_stride, const int64_t* slots,
+                                         uint8_t* cache, int64_t page_stride, int num_pages, hipStream_t stream) {
+  const int blocks = (num_tokens + 3) / 4;
+  hipLaunchKernelGGL(latent_cache_write_fp8_kernel, dim3(blocks), dim3(256), 0, stream, latent, latent_stride, rope,
+                     rope_stride, slots, cache, page_stride, num_pages, num_tokens);
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer_q_quant(int num_rows, const uint16_t* q, const float* w, uint8_t* codes, float* w_out,
                                   hipStream_t stream) {

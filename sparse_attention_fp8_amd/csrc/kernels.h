@@ -37,6 +37,15 @@ hipError_t launch_sparse_mla(const BatchArgs& batch, const uint16_t* q, int H, c
                              const MlaPlan& plan, uint16_t* out, float* lse, void* workspace,
                              hipStream_t stream);
 
+hipError_t launch_sparse_mla_fp8(const BatchArgs& batch, const uint16_t* q, int H, const uint8_t* kv8,
+                                 int64_t kv8_stride, const int32_t* indices, int k, float softmax_scale,
+                                 const MlaPlan& plan, uint16_t* out, float* lse, void* workspace,
+                                 hipStream_t stream);
+
+hipError_t launch_latent_cache_write_fp8(int num_tokens, const uint16_t* latent, int64_t latent_stride,
+                                         const uint16_t* rope, int64_t rope_stride, const int64_t* slots,
+                                         uint8_t* cache, int64_t page_stride, int num_pages, hipStream_t stream);
+
 hipError_t launch_indexer_q_quant(int num_rows, const uint16_t* q, const float* w, uint8_t* codes, float* w_out,
                                   hipStream_t stream);
 hipError_t launch_indexer_k_quant_cache(int num_tokens, const uint16_t* k, int64_t k_stride, const int64_t* slots,

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"dsa_indexer_logits_paged", "dsa_indexer_logits_prefill", "dsa_topk",
             "dsa_sparse_mla_decode", "dsa_indexer_q_quant_fp8", "dsa_indexer_k_quant_and_cache",
-            "dsa_latent_cache_write"} <= set(names)
+            "dsa_latent_cache_write", "dsa_sparse_mla_decode_fp8", "dsa_latent_cache_write_fp8"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -224,3 +224,25 @@ def test_latent_writer_rejects_bad_arguments(lib):
     assert b"kv_page_stride" in lib.dsa_last_error_message()
     assert latent_write(lib, rope=None) == ERR_NULL
     assert latent_write(lib, cache=FAKE + 8) == ERR_INVALID
+
+
+def test_fp8_latent_entries_reject_bad_arguments(lib):
+    b = batch()
+    f = lib.dsa_sparse_mla_decode_fp8
+    args = lambda **kw: dict(dict(q=FAKE, H=16, kv=FAKE, stride=41984, idx=FAKE, k=2048, sc=0.07, sp=1,
+                                  out=FAKE, lse=FAKE, ws=None, wsb=0), **kw)
+    call = lambda a: f(ctypes.byref(b), a["q"], a["H"], a["kv"], a["stride"], a["idx"], a["k"], a["sc"], a["sp"],
+                       a["out"], a["lse"], a["ws"], a["wsb"], None)
+    assert call(args(stride=41968)) == ERR_INVALID
+    assert b"kv_page_stride_bytes" in lib.dsa_last_error_message()
+    assert call(args(stride=41984 + 8)) == ERR_INVALID
+    assert call(args(H=48)) == ERR_UNSUPPORTED
+    assert call(args(kv=None)) == ERR_NULL
+    assert call(args(kv=FAKE + 8)) == ERR_INVALID
+    assert call(args(sp=4)) == ERR_WORKSPACE                   # split partials need a workspace
+    w = lib.dsa_latent_cache_write_fp8
+    assert w(0, None, 512, None, 64, None, None, 41984, 4, None) == OK
+    assert w(10, FAKE, 512, FAKE, 64, FAKE, FAKE, 8448, 4, None) == ERR_INVALID
+    assert w(10, FAKE, 500, FAKE, 64, FAKE, FAKE, 41984, 4, None) == ERR_INVALID
+    assert w(10, FAKE, 512, None, 64, FAKE, FAKE, 41984, 4, None) == ERR_NULL
+    assert w(-1, FAKE, 512, FAKE, 64, FAKE, FAKE, 41984, 4, None) == ERR_UNSUPPORTED
