@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="latent cache of the step's sparse MLA (fp8: e4m3 latent in 4 scaled groups + bf16 rope)")
     return ap.parse_args()
 
 
@@ -55,7 +57,9 @@ def algorithmic_bytes(wl):
     logit_bytes = int(4 * ext.sum())
     sel = np.minimum(ext, k)
     mla = int((1152 * sel + 4 * k + H * (1152 + 1024 + 4)).sum())
+    mla8 = int((656 * sel + 4 * k + H * (1152 + 1024 + 4)).sum())
     return {"indexer": idx_in + logit_bytes, "topk": logit_bytes + 4 * k * len(ext), "sparse_mla": mla,
+            "sparse_mla_fp8": mla8,
             "indexer_flops": int(16384 * ext.sum()),
             "mla_flops": int(2 * H * (576 + 512) * sel.sum())}
 
@@ -72,15 +76,16 @@ def _row_extents(seq_lens, qs):
     return seq, ext
 
 
-STAGE_SOURCES = {"indexer": "indexer_paged.hip", "indexer_prefill": "indexer_prefill.hip",
-                 "topk": "topk.hip", "sparse_mla": "sparse_mla.hip"}
+STAGE_SOURCES = {"indexer": ("indexer_paged.hip",), "indexer_prefill": ("indexer_prefill.hip",),
+                 "topk": ("topk.hip",), "sparse_mla": ("sparse_mla.hip", "mla_common.h"),
+                 "sparse_mla_fp8": ("sparse_mla_fp8.hip", "mla_common.h")}
 
 
 def stage_source_sha(stage):
-    """sha256 prefix of the kernel sources of one stage (its file + common.h)."""
+    """sha256 prefix of the kernel sources of one stage (its files + common.h)."""
     import hashlib
     m = hashlib.sha256()
-    for f in (STAGE_SOURCES[stage], "common.h"):
+    for f in STAGE_SOURCES[stage] + ("common.h",):
         with open(os.path.join(ROOT, "sparse_attention_fp8_amd", "csrc", f), "rb") as fh:
             m.update(fh.read())
     return m.hexdigest()[:16]
@@ -214,6 +219,13 @@ def main():
     sets = []
     base = {"q_fp8": wl.q_fp8.to(dev), "weights": wl.weights.to(dev), "idx_cache": wl.idx_cache.to(dev),
             "q_mla": wl.q_mla.to(dev), "kv_cache": wl.kv_cache.to(dev)}
+    # the fp8 latent cache of the same rows, written by the library's own writer
+    num_slots = wl.num_pages * 64
+    kv8 = torch.zeros(wl.num_pages, dsa.binding.KV8_PAGE_BYTES, dtype=torch.uint8, device=dev)
+    rows = base["kv_cache"][:, :64 * 576].reshape(num_slots, 576)
+    dsa.latent_cache_write_fp8(rows[:, :512], rows[:, 512:], torch.arange(num_slots, dtype=torch.int64, device=dev),
+                               kv8)
+    base["kv8"] = kv8
     sets.append(base)
     for _ in range(copies - 1):
         sets.append({n: t.clone() for n, t in base.items()})
@@ -234,11 +246,16 @@ def main():
             indexer(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=False)
         elif name == "topk":
             dsa.topk(batch, logits, indices, k=k, workspace=ws_topk)
+        elif name == "sparse_mla_fp8":
+            dsa.sparse_mla_decode_fp8(batch, t["q_mla"], t["kv8"], indices, wl.softmax_scale, out, lse,
+                                      num_splits=args.splits, workspace=ws_mla)
         else:
             dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
                                   num_splits=args.splits, workspace=ws_mla)
 
-    stages = ("indexer", "topk", "sparse_mla")
+    mla_stage = "sparse_mla_fp8" if args.kv == "fp8" else "sparse_mla"
+    stages = ("indexer", "topk", mla_stage)
+    other_mla = "sparse_mla" if args.kv == "fp8" else "sparse_mla_fp8"
 
     def step(i):
         for name in stages:
@@ -261,7 +278,7 @@ def main():
     # the stage's average launch duration is measured on its own stream.
     reps = 2 * copies
     stage_graphs = {}
-    for name in stages:
+    for name in stages + (other_mla,):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(reps):
@@ -283,7 +300,7 @@ def main():
 
     stage_ms = {}
     stage_rounds = max(1, args.steps // reps)
-    for name in stages:
+    for name in stages + (other_mla,):
         stage_graphs[name].replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -306,7 +323,8 @@ def main():
     copy_gbs = 5 * 2 * cbuf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del cbuf, cdst
 
-    total_bytes = nbytes["indexer"] + nbytes["topk"] + nbytes["sparse_mla"]
+    alt_ms = stage_ms.pop(other_mla)
+    total_bytes = nbytes["indexer"] + nbytes["topk"] + nbytes[mla_stage]
     if prefill:
         dom = "indexer"
         achieved = nbytes["indexer_flops"] / (stage_ms[dom] * 1e-3) / 1e12
@@ -321,6 +339,7 @@ def main():
                 "per_launch": f"{nbytes[dom]} B"}
     line = {
         "metric": "DSA decode steps/s (indexer+topk+sparse MLA) and % of HBM roofline at 1 GPU",
+        "kv_cache": args.kv,
         "value": 1000.0 / ms,
         "unit": "steps/s",
         "n_gpus": 1,
@@ -330,7 +349,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8 indexer / bf16 MLA, fp32 accumulate",
+        "dtype": "fp8 indexer / bf16 MLA, fp32 accumulate" if args.kv == "bf16"
+                 else "fp8 indexer / fp8-cache MLA (bf16 operands), fp32 accumulate",
         "data": "synthetic",
         "config": {"workload": synth.CONFIGS[args.config], "name": args.config, "rows": R, "mla_heads": H,
                    "topk": k, "splits": splits, "cache_copies": copies,
@@ -344,6 +364,10 @@ def main():
                   f"{reps} launches of one entry point",
         "rows_per_s": R * 1000.0 / ms,
     }
+    line["other_kv_stage"] = {"stage": other_mla, "us": alt_ms * 1e3, "bytes": nbytes[other_mla],
+                              "GBps": nbytes[other_mla] / (alt_ms * 1e-3) / 1e9,
+                              "hbm_frac": nbytes[other_mla] / (alt_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "note": "the same indices through the other latent-cache format"}
     line["pre_path"] = pre_path(dsa, wl, batch, base, dev, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)

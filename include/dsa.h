@@ -203,6 +203,7 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
  *  kv_cache_fp8          fp8 latent pages, 16-byte aligned
  *  kv_page_stride_bytes  >= DSA_KV8_PAGE_BYTES, a multiple of 16 (128 keeps
  *                        every row on whole 128-byte lines)
+ *  batch->num_pages      at most 2^25 (UNSUPPORTED above)
  */
 int dsa_sparse_mla_decode_fp8(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads,
                               const uint8_t* kv_cache_fp8, int64_t kv_page_stride_bytes, const int32_t* indices,

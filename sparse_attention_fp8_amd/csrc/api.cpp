@@ -22,6 +22,9 @@ constexpr int kTargetCUs = 256;
 // every grid far inside the 2^31 workgroup limit).
 constexpr int kMaxWriteItems = DSA_MAX_WRITE_ITEMS;
 
+// The fp8 sparse MLA keeps a token's cache slot (page * 64 + slot) in 32 bits.
+constexpr int kMaxKv8Pages = 1 << 25;
+
 thread_local std::string g_last_error;
 
 int fail(int status, const char* fmt, ...) {
@@ -237,6 +240,8 @@ int dsa_sparse_mla_decode_fp8(const dsa_batch_t* batch, const uint16_t* q, int32
                 (long long)kv_page_stride_bytes, DSA_KV8_PAGE_BYTES);
   if (!std::isfinite(softmax_scale)) return fail(DSA_ERR_INVALID, "softmax_scale is not finite");
   if (num_splits < 0) return fail(DSA_ERR_INVALID, "num_splits=%d < 0", num_splits);
+  if (batch->num_pages > kMaxKv8Pages)
+    return fail(DSA_ERR_UNSUPPORTED, "num_pages=%d above %d for the fp8 latent cache", batch->num_pages, kMaxKv8Pages);
   if (batch->num_rows == 0) return ok();
   if (!q || !indices || !out || !lse) return fail(DSA_ERR_NULL, "q, indices, out and lse must not be NULL");
   if (!aligned(q, 16) || !aligned(out, 16)) return fail(DSA_ERR_INVALID, "q and out must be 16-byte aligned");

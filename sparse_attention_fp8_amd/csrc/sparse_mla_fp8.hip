@@ -76,15 +76,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
 }
 
+constexpr int kMaxTiles8 = DSA_MAX_TOPK / kTile8;   // 32 tiles per split at most
+constexpr int kDeepTiles = 8;                        // tiles per split from which two stay in flight
+
+// Tile buffers: three (two 41 KB tiles in flight while one is multiplied) when
+// the head block's P' fits beside them, else two.
+template <int HT>
+struct MlaBuffers8 {
+  static constexpr int value = HT <= 2 ? 3 : 2;
+};
+
 template <int HT, int TP>
 struct MlaShared8 {
-  unsigned char tile[2][kTileBytes8];                // double-buffered gathered rows
-  const unsigned char* rowptr[2][kTile8];            // source row of each slot
-  const unsigned char* sptr[2][kTile8];              // source scale record of each slot
-  uint64_t mask[2];                                   // valid slots of each buffer
-  alignas(16) uint16_t p[HT][4][16][kPStride];       // bf16 p * scale_g [tile][group][head][token]
-  float tmax[HT][TP][16];                             // per-part tile maxima
+  unsigned char tile[MlaBuffers8<HT>::value][kTileBytes8];   // gathered rows, ring of buffers
+  int slot[kMaxTiles8 * kTile8];                             // cache slot (page * 64 + s) or -1
+  uint64_t mask[kMaxTiles8];                                  // valid slots of each tile
+  alignas(16) uint16_t p[HT][4][16][kPStride];                // bf16 p * scale_g [tile][group][head][token]
+  float tmax[HT][TP][16];                                     // per-part tile maxima
 };
+
+// s_waitcnt that waits until at most n vector-memory loads of this wave are
+// outstanding (n < 64), leaving the LDS and export counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Byte offset inside a tile of the 16-byte slot `slot` of token `tok`, column
 // group `cg`.
@@ -102,7 +119,11 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   constexpr int NG = DW / 128;         // scale groups per wave's dims
   constexpr int RGW = kRg8 / NW;       // row groups each wave gathers
   static_assert(RGW * NW == kRg8, "waves must split the row groups evenly");
+  constexpr int NBUF = MlaBuffers8<HT>::value;
+  constexpr int DEPTH = NBUF - 1;      // tiles in flight while one is multiplied
   constexpr int SCALE_WAVE = NW - 1;   // the wave that also copies the scale records
+  constexpr int NDR = RGW * kCg8;      // row loads per wave and tile
+  constexpr int ND = NDR + 1;          // + the scale load (scale wave only)
   __shared__ MlaShared8<HT, TP> sh;
 
   const int R = a.batch.num_rows;
@@ -126,40 +147,61 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   const int slot1 = min(slot0 + a.split_slots, a.k);
   const int ntiles = (slot1 - slot0 + kTile8 - 1) / kTile8;
 
-  // Row and scale pointers of slot j (wave 0 only): index -> block table -> page.
-  const int32_t* idx_row = a.indices + (int64_t)r * a.k;
-  auto load_idx = [&](int t) -> int {
-    const int j = slot0 + t * kTile8 + lane;
-    return (t < ntiles && j < slot1) ? idx_row[j] : -1;
-  };
-  int b = -1, e = 0;
-  auto load_page = [&](int idx) -> int {
-    return (b >= 0 && idx >= 0 && idx < a.batch.max_seq_len)
-               ? a.batch.block_table[(int64_t)b * a.batch.bt_stride + (idx >> 6)] : -1;
-  };
-  auto publish = [&](int t, int idx, int page) {
-    const bool valid = idx >= 0 && idx < e && page >= 0 && page < a.batch.num_pages;
-    const unsigned char* row = reinterpret_cast<const unsigned char*>(g_zero_row8);
-    const unsigned char* sc = row;
-    if (valid) {
-      const unsigned char* pg = a.kv8 + (int64_t)page * a.kv8_stride;
-      row = pg + (idx & 63) * kRow8;
-      sc = pg + kScaleOff8 + (idx & 63) * 16;
+  uint4 qreg[18];
+  // Prologue.  Every wave turns its tiles' indices into cache slots: tile t
+  // belongs to wave t % NW, its entry lane to this lane.  All index loads go
+  // out with the sequence search, then all block-table loads, so the chain is
+  // two round trips whatever the number of tiles.  A slot is -1 when the index
+  // is padding, outside [0, e_r) or on a page outside the cache.
+  {
+    constexpr int MT = kMaxTiles8 / NW;
+    const int32_t* idx_row = a.indices + (int64_t)r * a.k;
+    int idx[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int t = wave + NW * m;
+      const int j = slot0 + t * kTile8 + lane;
+      idx[m] = (t < ntiles && j < slot1) ? idx_row[j] : -1;
     }
-    sh.rowptr[t & 1][lane] = row;
-    sh.sptr[t & 1][lane] = sc;
-    const uint64_t m = __ballot(valid);
-    if (lane == 0) sh.mask[t & 1] = t < ntiles ? m : 0ull;
-  };
-  // Gather of tile t into buffer t & 1: one wave-wide load fills one 1 KB
+    const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
+    // The table needs only idx < max_seq_len to stay inside the row; e and the
+    // page range are checked below.
+    int page[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+      page[m] = (b >= 0 && idx[m] >= 0 && idx[m] < a.batch.max_seq_len)
+                    ? a.batch.block_table[(int64_t)b * a.batch.bt_stride + (idx[m] >> 6)] : -1;
+    const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;   // rides with the block-table loads
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int t = wave + NW * m;
+      if (t < ntiles) {
+        const bool valid = idx[m] < e && page[m] >= 0 && page[m] < a.batch.num_pages;
+        sh.slot[t * kTile8 + lane] = valid ? page[m] * kPage + (idx[m] & 63) : -1;
+        const uint64_t msk = __ballot(valid);
+        if (lane == 0) sh.mask[t] = msk;
+      }
+    }
+  }
+  __syncthreads();                                   // slots and masks of every tile published
+
+  // Gather of tile t into buffer t % NBUF: one wave-wide load fills one 1 KB
   // block; lane l copies slot l & 7 of row l >> 3 (chunk (l & 7) ^ r8 ^ (rg & 1)
   // of that row's 128-byte column group).  The scale wave adds one load of the
-  // 64 scale records (lane l: token l).
-  constexpr int NDR = RGW * kCg8;                      // row loads per wave and tile
-  constexpr int ND = NDR + (1);                        // + the scale load (scale wave only)
+  // 64 scale records (lane l: token l).  Every tile is gathered (masked slots
+  // read a static zero row), so each wave issues the same number of loads per
+  // tile and the in-flight count below is exact.
   auto gather_src = [&](int t, int j) -> const unsigned char* {
     const int rg = wave * RGW + j;
-    return sh.rowptr[t & 1][rg * 8 + (lane >> 3)] + (((lane & 7) ^ (lane >> 3) ^ (rg & 1)) << 4);
+    const int sl = sh.slot[t * kTile8 + rg * 8 + (lane >> 3)];
+    const unsigned char* row = sl >= 0 ? a.kv8 + (int64_t)(sl >> 6) * a.kv8_stride + (sl & 63) * kRow8
+                                       : reinterpret_cast<const unsigned char*>(g_zero_row8);
+    return row + (((lane & 7) ^ (lane >> 3) ^ (rg & 1)) << 4);
+  };
+  auto scale_src = [&](int t) -> const unsigned char* {
+    const int sl = sh.slot[t * kTile8 + lane];
+    return sl >= 0 ? a.kv8 + (int64_t)(sl >> 6) * a.kv8_stride + kScaleOff8 + (sl & 63) * 16
+                   : reinterpret_cast<const unsigned char*>(g_zero_row8);
   };
   auto gather_one = [&](const unsigned char* const* src, const unsigned char* ssrc, uint32_t dst, int i) {
     if (i < NDR) {
@@ -169,23 +211,25 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
       lds_dma16(ssrc, dst + kTileScaleOff);
     }
   };
-
-  // Prologue: wave 0's dependent chain first, then the q loads.
-  int idx_next = -1;
-  if (wave == 0) {
-    const int i0 = load_idx(0), i1 = load_idx(1);
-    idx_next = load_idx(2);
-    b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
-    e = b >= 0 ? row_extent(a.batch, b, r) : 0;
-    const int p0 = load_page(i0), p1 = load_page(i1);
-    publish(0, i0, p0);
-    publish(1, i1, p1);
-  }
-  asm volatile("" ::: "memory");
+  auto gather_all = [&](int t) __attribute__((always_inline)) {
+    const unsigned char* src[RGW];
+#pragma unroll
+    for (int j = 0; j < RGW; ++j) src[j] = gather_src(t, j);
+    const unsigned char* ssrc = scale_src(t);
+    const uint32_t dst = lds_addr(sh.tile[t % NBUF]);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) gather_one(src, ssrc, dst, i);
+  };
+  // Two tiles in flight pay off only once the pipeline runs for a while: with a
+  // few tiles per split, asking for two at once delays the first.
+  const int depth = (DEPTH > 1 && ntiles >= kDeepTiles) ? DEPTH : 1;
+  // Tile 0's copy goes out first, then q, which arrives while the copy is in
+  // flight; one wait then covers both, so inside the loop no load but the
+  // copies is ever outstanding and the waits there count copies only.
+  if (ntiles > 0) gather_all(0);
   // q operands.  Latent pair j (dims 64 j .. 64 j + 63): MFMA 2 j takes dims
   // 64 j + 16 g + 0..7, MFMA 2 j + 1 dims 64 j + 16 g + 8..15 (the k order the
   // 128-bit code reads deliver).  Rope step s: dims 512 + 32 s + 8 g + 0..7.
-  uint4 qreg[18];
   {
     const uint16_t* qp = a.q + ((int64_t)r * a.H + h) * kKvDim;
 #pragma unroll
@@ -196,17 +240,10 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
     qreg[16] = *reinterpret_cast<const uint4*>(qp + kVDim + 8 * g);
     qreg[17] = *reinterpret_cast<const uint4*>(qp + kVDim + 32 + 8 * g);
   }
-  __syncthreads();
-  auto gather_all = [&](int t) __attribute__((always_inline)) {
-    const unsigned char* src[RGW];
+  wait_vmcnt<0>();
 #pragma unroll
-    for (int j = 0; j < RGW; ++j) src[j] = gather_src(t, j);
-    const unsigned char* ssrc = sh.sptr[t & 1][lane];
-    const uint32_t dst = lds_addr(sh.tile[t & 1]);
-#pragma unroll
-    for (int i = 0; i < ND; ++i) gather_one(src, ssrc, dst, i);
-  };
-  if (sh.mask[0] != 0ull) gather_all(0);
+  for (int t = 1; t < DEPTH; ++t)
+    if (t < depth && t < ntiles) gather_all(t);
 
   // PV read address parts: lane i of group g addresses token 8 g + i / 2 of
   // the 32-token step, bytes 16 (dim tile % 8) + 8 (i % 2) of its column group.
@@ -220,23 +257,25 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   float l_part = 0.f;
 
   for (int t = 0; t < ntiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();                                   // tile t landed; pointers of t + 1 ready
-    const uint64_t mask = sh.mask[t & 1];
-    int idx_cur = -1, page_cur = -1;
-    if (wave == 0) {
-      idx_cur = idx_next;
-      page_cur = load_page(idx_cur);
+    // Wait for this wave's copies of tile t: the copies of the DEPTH - 1 later
+    // tiles already issued may stay in flight.
+    if (DEPTH > 1 && depth > 1 && t + 1 < ntiles) {
+      if (wave == SCALE_WAVE) wait_vmcnt<(DEPTH - 1) * (NDR + 1)>();
+      else wait_vmcnt<(DEPTH - 1) * NDR>();
+    } else {
+      wait_vmcnt<0>();
     }
-    if (wave == 0) idx_next = load_idx(t + 3);
-    const bool pre = t + 1 < ntiles && sh.mask[(t + 1) & 1] != 0ull;
+    __syncthreads();                                   // tile t landed in every wave; buffer (t + depth) % NBUF is free
+    const uint64_t mask = sh.mask[t];
+    const int tn = t + depth;                          // the tile whose copy starts now
+    const bool pre = tn < ntiles;
     const unsigned char* gsrc[RGW];
     const unsigned char* gssrc = nullptr;
-    const uint32_t gdst = lds_addr(sh.tile[(t + 1) & 1]);
+    const uint32_t gdst = lds_addr(sh.tile[tn % NBUF]);
     if (pre) {
 #pragma unroll
-      for (int j = 0; j < RGW; ++j) gsrc[j] = gather_src(t + 1, j);
-      gssrc = sh.sptr[(t + 1) & 1][lane];
+      for (int j = 0; j < RGW; ++j) gsrc[j] = gather_src(tn, j);
+      gssrc = scale_src(tn);
     }
     if (pre && mask == 0ull) {
 #pragma unroll
@@ -244,7 +283,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
     }
 
     if (mask != 0ull) {
-      const unsigned char* tile = sh.tile[t & 1];
+      const unsigned char* tile = sh.tile[t % NBUF];
       float z[TPT][4];
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
@@ -357,7 +396,6 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
         }
       }
     }
-    if (wave == 0) publish(t + 2, idx_cur, page_cur);
   }
 
   float l_tot = l_part + __shfl_xor(l_part, 16, 64);
