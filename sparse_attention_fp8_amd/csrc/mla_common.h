@@ -60,14 +60,25 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
 }
 
 // N-way merge of the split partials: one wave per (row, head), 8 dims per lane.
-// The split maxima and sums are read lane-parallel (lane i <-> split i), and
-// the accumulator loads of all splits are issued before they are combined.
+// Every load goes out before any is used -- the split maxima and sums
+// (lane-parallel, lane i <-> split i) and the accumulators of the first U
+// splits -- so the merge costs one memory round trip, not two.
 __global__ void __launch_bounds__(256) sparse_mla_merge_kernel(MlaArgs a) {
   const int R = a.batch.num_rows;
   const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (int64_t)R * a.H) return;
   const int lane = lane_id();
   const int64_t RH = (int64_t)R * a.H;
+  constexpr int U = 8;
+  float4 x[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u < a.splits) {
+      const float4* src = reinterpret_cast<const float4*>(a.part_acc + (u * RH + pair) * kVDim + 8 * lane);
+      x[u][0] = src[0];
+      x[u][1] = src[1];
+    }
+  }
   float mi = kMaskSentinel, li = 0.f;
   if (lane < a.splits) {
     mi = a.part_ml[(lane * RH + pair) * 2];
@@ -77,15 +88,16 @@ __global__ void __launch_bounds__(256) sparse_mla_merge_kernel(MlaArgs a) {
   const float wi = li > 0.f ? exp2f(mi - M) : 0.f;
   const float L = wave_sum(li * wi);
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 8;
   for (int i0 = 0; i0 < a.splits; i0 += U) {
-    float4 x[U][2];
+    if (i0 > 0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (i0 + u < a.splits) {
-        const float4* src = reinterpret_cast<const float4*>(a.part_acc + ((i0 + u) * RH + pair) * kVDim + 8 * lane);
-        x[u][0] = src[0];
-        x[u][1] = src[1];
+      for (int u = 0; u < U; ++u) {
+        if (i0 + u < a.splits) {
+          const float4* src =
+              reinterpret_cast<const float4*>(a.part_acc + ((i0 + u) * RH + pair) * kVDim + 8 * lane);
+          x[u][0] = src[0];
+          x[u][1] = src[1];
+        }
       }
     }
 #pragma unroll
