@@ -45,6 +45,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 32768;          // keys per workgroup in the row pass
 constexpr int kMergeMax = 65536;       // candidates per row in the merge pass
+constexpr int kGroupChunks = 4;        // chunks one group merge reduces to k candidates
 constexpr int kBins = 2048;
 constexpr int kCopies = 8;             // interleaved copies of the pass-one histogram
 constexpr int kCand = 4096;            // LDS list for the threshold bin's keys
@@ -59,6 +60,10 @@ struct TopkArgs {
   uint32_t* cand_keys;    // [R, nchunks, k]
   int32_t* cand_idx;      // [R, nchunks, k]
   int32_t* cand_count;    // [R, nchunks]
+  int ngroups;            // ceil(nchunks / kGroupChunks) when the merge has two levels, else 0
+  uint32_t* grp_keys;     // [R, ngroups, k]
+  int32_t* grp_idx;       // [R, ngroups, k]
+  int32_t* grp_count;     // [R, ngroups]
 };
 
 // Selection state of one workgroup.  hist1 is pass one's histogram, bin-major
@@ -412,6 +417,54 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
   if (threadIdx.x == 0) a.cand_count[slot] = k;
 }
 
+// First level of the merge for rows of more than kGroupChunks chunks: group g
+// of row r reduces the candidates of chunks [4 g, 4 g + 4) to its top k, kept
+// in ascending candidate order (= ascending key index), so the final level
+// sees the same tie order.  Exact by the chunking argument once more: a key of
+// the row's top k is in the top k of its group.
+template <int KPT>
+__global__ void __launch_bounds__(kThreads) topk_group_kernel(TopkArgs a) {
+  __shared__ Shared sh;
+  const int r = blockIdx.x / a.ngroups;
+  const int g = blockIdx.x % a.ngroups;
+  const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
+  const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
+  const int k = a.k;
+  const int nch = (e + kChunk - 1) / kChunk;
+  const int c0 = g * kGroupChunks;
+  const int64_t gslot = (int64_t)r * a.ngroups + g;
+  if (e <= kChunk * kGroupChunks || c0 >= nch) {
+    if (threadIdx.x == 0) a.grp_count[gslot] = 0;
+    return;
+  }
+  const int c1 = min(c0 + kGroupChunks, nch);
+  // chunks before the row's last hold exactly k candidates, so the group's
+  // candidates are contiguous
+  const int64_t row_slot = (int64_t)r * a.nchunks;
+  const int n = (c1 - c0 - 1) * k + a.cand_count[row_slot + c1 - 1];
+  const uint32_t* ck = a.cand_keys + (row_slot + c0) * k;
+  const int32_t* ci = a.cand_idx + (row_slot + c0) * k;
+  uint32_t* gk = a.grp_keys + gslot * k;
+  int32_t* gi = a.grp_idx + gslot * k;
+  if (n <= k) {
+    for (int i = threadIdx.x; i < n; i += kThreads) { gk[i] = ck[i]; gi[i] = ci[i]; }
+    if (threadIdx.x == 0) a.grp_count[gslot] = n;
+    return;
+  }
+  Keys<KPT> keys;
+  load_raw_keys(keys, ck, n);
+  const Selection sel = radix_select(keys, k, sh);
+  stage_selected(keys, sel, k, sh);
+  for (int i = threadIdx.x; i < k; i += kThreads) {
+    const int p = sh.out[i];
+    gk[i] = p >= 0 ? ck[p] : 0u;
+    gi[i] = p >= 0 ? ci[p] : -1;
+  }
+  if (threadIdx.x == 0) a.grp_count[gslot] = k;
+}
+
+// Final selection of a multi-chunk row over the chunk candidates, or over the
+// group candidates when the merge has two levels.
 template <int KPT>
 __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
   __shared__ Shared sh;
@@ -421,12 +474,23 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
   if (e <= kChunk) return;
   const int k = a.k;
   const int nch = (e + kChunk - 1) / kChunk;
-  // Every chunk but the last is full (kChunk >= k keys -> exactly k winners),
-  // so the candidates of row r are contiguous: (nch - 1) * k + count_last.
-  const int64_t row_slot = (int64_t)r * a.nchunks;
-  const int n = (nch - 1) * k + a.cand_count[row_slot + nch - 1];
-  const uint32_t* ck = a.cand_keys + row_slot * k;
-  const int32_t* ci = a.cand_idx + row_slot * k;
+  // Every chunk (group) but the last is full (exactly k winners), so the
+  // candidates of row r are contiguous: (units - 1) * k + count_last.
+  const uint32_t* ck;
+  const int32_t* ci;
+  int n;
+  if (a.ngroups > 0 && nch > kGroupChunks) {
+    const int ng = (nch + kGroupChunks - 1) / kGroupChunks;
+    const int64_t row_slot = (int64_t)r * a.ngroups;
+    n = (ng - 1) * k + a.grp_count[row_slot + ng - 1];
+    ck = a.grp_keys + row_slot * k;
+    ci = a.grp_idx + row_slot * k;
+  } else {
+    const int64_t row_slot = (int64_t)r * a.nchunks;
+    n = (nch - 1) * k + a.cand_count[row_slot + nch - 1];
+    ck = a.cand_keys + row_slot * k;
+    ci = a.cand_idx + row_slot * k;
+  }
   int32_t* out = a.indices + (int64_t)r * k;
   Keys<KPT> keys;
   load_raw_keys(keys, ck, n);
@@ -442,7 +506,14 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
 
 int topk_num_chunks(int max_seq_len) { return max_seq_len <= kChunk ? 1 : (max_seq_len + kChunk - 1) / kChunk; }
 
-int64_t topk_max_seq_len(int k) { return (int64_t)(kMergeMax / k) * kChunk; }
+// Rows of up to kGroupChunks chunks merge in one level (candidates <=
+// kGroupChunks * k), longer rows in two (final candidates <= groups * k).
+int topk_num_groups(int max_seq_len) {
+  const int nch = topk_num_chunks(max_seq_len);
+  return nch > kGroupChunks ? (nch + kGroupChunks - 1) / kGroupChunks : 0;
+}
+
+int64_t topk_max_seq_len(int k) { return (int64_t)(kMergeMax / k) * kGroupChunks * kChunk; }
 
 size_t topk_workspace_bytes(int num_rows, int max_seq_len, int k) {
   const int nch = topk_num_chunks(max_seq_len);
@@ -451,7 +522,16 @@ size_t topk_workspace_bytes(int num_rows, int max_seq_len, int k) {
   size_t bytes = slots * (size_t)k * 8;     // keys + indices
   bytes = (bytes + 255) & ~(size_t)255;
   bytes += slots * 4;                       // counts
-  return (bytes + 255) & ~(size_t)255;
+  bytes = (bytes + 255) & ~(size_t)255;
+  const int ng = topk_num_groups(max_seq_len);
+  if (ng > 0) {
+    const size_t gslots = (size_t)num_rows * ng;
+    bytes += gslots * (size_t)k * 8;        // group keys + indices
+    bytes = (bytes + 255) & ~(size_t)255;
+    bytes += gslots * 4;                    // group counts
+    bytes = (bytes + 255) & ~(size_t)255;
+  }
+  return bytes;
 }
 
 hipError_t launch_topk(const BatchArgs& batch, const float* logits, int64_t logits_stride, int k,
@@ -471,6 +551,15 @@ hipError_t launch_topk(const BatchArgs& batch, const float* logits, int64_t logi
     a.cand_idx = reinterpret_cast<int32_t*>(ws + slots * (size_t)k * 4);
     size_t off = (slots * (size_t)k * 8 + 255) & ~(size_t)255;
     a.cand_count = reinterpret_cast<int32_t*>(ws + off);
+    off = (off + slots * 4 + 255) & ~(size_t)255;
+    a.ngroups = topk_num_groups(batch.max_seq_len);
+    if (a.ngroups > 0) {
+      const size_t gslots = (size_t)batch.num_rows * a.ngroups;
+      a.grp_keys = reinterpret_cast<uint32_t*>(ws + off);
+      a.grp_idx = reinterpret_cast<int32_t*>(ws + off + gslots * (size_t)k * 4);
+      off = (off + gslots * (size_t)k * 8 + 255) & ~(size_t)255;
+      a.grp_count = reinterpret_cast<int32_t*>(ws + off);
+    }
   }
   // keys per thread: the smallest of 8 / 16 / 32 that covers a chunk
   const int longest = a.nchunks > 1 ? kChunk : batch.max_seq_len;
@@ -484,9 +573,18 @@ hipError_t launch_topk(const BatchArgs& batch, const float* logits, int64_t logi
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.nchunks <= 1) return err;
-  const int64_t cands = (int64_t)a.nchunks * k;
+  if (a.ngroups > 0) {
+    // a group holds kGroupChunks * k <= 8192 candidates (k <= 2048)
+    hipLaunchKernelGGL(topk_group_kernel<8>, dim3((unsigned)((int64_t)batch.num_rows * a.ngroups)), dim3(kThreads),
+                       0, stream, a);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int64_t cands = (int64_t)(a.ngroups > 0 ? a.ngroups : a.nchunks) * k;
   if (cands <= 8 * kThreads) {
     hipLaunchKernelGGL(topk_merge_kernel<8>, dim3((unsigned)batch.num_rows), dim3(kThreads), 0, stream, a);
+  } else if (cands <= 16 * kThreads) {
+    hipLaunchKernelGGL(topk_merge_kernel<16>, dim3((unsigned)batch.num_rows), dim3(kThreads), 0, stream, a);
   } else if (cands <= 32 * kThreads) {
     hipLaunchKernelGGL(topk_merge_kernel<32>, dim3((unsigned)batch.num_rows), dim3(kThreads), 0, stream, a);
   } else {

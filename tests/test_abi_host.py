@@ -115,6 +115,19 @@ def test_topk_workspace_sizes(lib):
     need = lib.dsa_topk_workspace_bytes(ctypes.byref(b), 2048)
     assert need >= 4096 * 2 * 2048 * 8 and need % 256 == 0      # two 32768-key chunks per row
     assert lib.dsa_topk_workspace_bytes(None, 2048) == 0
+    # past four chunks the merge adds a level: groups of four chunks keep k each
+    one_m = batch(max_seq_len=1 << 20, bt_stride=1 << 14, num_rows=2)
+    need = lib.dsa_topk_workspace_bytes(ctypes.byref(one_m), 2048)
+    assert need >= 2 * 32 * 2048 * 8 + 2 * 8 * 2048 * 8 and need % 256 == 0
+
+
+def test_topk_longest_row(lib):
+    ok_len, too_long = 4 * 1024 * 1024, 4 * 1024 * 1024 + 1
+    b = batch(max_seq_len=ok_len, bt_stride=ok_len // 64)
+    assert lib.dsa_topk_workspace_bytes(ctypes.byref(b), 2048) > 0
+    assert topk_call(lib, batch(max_seq_len=too_long, bt_stride=too_long // 64 + 1), stride=too_long + 3) \
+        == ERR_UNSUPPORTED
+    assert b"max_seq_len" in lib.dsa_last_error_message()
 
 
 def mla_call(lib, b, H=16, k=2048, splits=0, ws=FAKE, ws_bytes=1 << 40, **kw):

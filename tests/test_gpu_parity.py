@@ -202,10 +202,11 @@ def test_topk_forced_ties(dsa, pool):
     check_topk(got, host, wl, 2048)
 
 
-@pytest.mark.parametrize("L", [600_000, 140_000])
+@pytest.mark.parametrize("L", [2_000_000, 600_000, 140_000])
 def test_topk_long_rows_merge(dsa, L):
-    """Rows far past one 32768-key chunk: many chunks feed the candidate merge
-    (for 600k keys it holds over 32768 candidates); values repeat heavily."""
+    """Rows far past one 32768-key chunk: many chunks feed the candidate merge,
+    through a group level past four chunks (2M keys: 62 chunks, 16 groups);
+    values repeat heavily, so ties decide much of the selection."""
     import sparse_attention_fp8_amd as lib
     lens = [L, L - 1000, 5000]
     qs = [0, 1, 2, 3]
