@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import sparse_attention_fp8_amd as dsa
 from sparse_attention_fp8_amd import synth
 
@@ -23,7 +24,17 @@ from test_gpu_parity import DEV, check_logits, check_mla, mla_oracle, oracle_ind
 pytestmark = pytest.mark.gpu
 
 
-def sub_workload(wl, seqs, perm_seed=None):
+def kv8_cache(wl):
+    """The fp8 latent cache of every slot of wl's bf16 cache, written on the GPU."""
+    slots = wl.num_pages * 64
+    rows = wl.kv_cache[:, :64 * 576].reshape(slots, 576).to(DEV)
+    kv8 = torch.zeros(wl.num_pages, dsa.binding.KV8_PAGE_BYTES, dtype=torch.uint8, device=DEV)
+    dsa.latent_cache_write_fp8(rows[:, :512], rows[:, 512:], torch.arange(slots, dtype=torch.int64, device=DEV), kv8)
+    torch.cuda.synchronize()
+    return kv8.cpu()
+
+
+def sub_workload(wl, seqs, perm_seed=None, kv8=None):
     """The sequences `seqs` of `wl` (in that order) as a workload of their own,
     sharing wl's caches; with perm_seed the physical pages are renumbered by a
     random permutation (caches permuted to match)."""
@@ -40,11 +51,15 @@ def sub_workload(wl, seqs, perm_seed=None):
         bt = perm[bt]
         idx_cache = idx_cache[torch.from_numpy(inv)]
         kv_cache = kv_cache[torch.from_numpy(inv)]
+        if kv8 is not None:
+            kv8 = kv8[torch.from_numpy(inv)]
     sl = wl.seq_lens.numpy()[seqs]
     batch = dsa.Batch.from_host(torch.from_numpy(sl.copy()), torch.from_numpy(query_start),
                                 torch.from_numpy(np.ascontiguousarray(bt)), wl.num_pages, device=DEV)
     t = {"q_fp8": wl.q_fp8[rows].to(DEV), "weights": wl.weights[rows].to(DEV), "q_mla": wl.q_mla[rows].to(DEV),
          "idx_cache": idx_cache.to(DEV), "kv_cache": kv_cache.to(DEV)}
+    if kv8 is not None:
+        t["kv8"] = kv8.to(DEV)
     return batch, t, rows
 
 
@@ -58,7 +73,12 @@ def run(batch, t, wl, prefill, splits):
     fn = dsa.indexer_logits_prefill if prefill else dsa.indexer_logits_paged
     fn(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=True)
     dsa.topk(batch, logits, indices, k=k)
-    dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse, num_splits=splits)
+    if "kv8" in t:
+        dsa.sparse_mla_decode_fp8(batch, t["q_mla"], t["kv8"], indices, wl.softmax_scale, out, lse,
+                                  num_splits=splits)
+    else:
+        dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
+                              num_splits=splits)
     torch.cuda.synchronize()
     return (logits.cpu().numpy(), indices.cpu().numpy(), out.view(torch.int16).cpu().numpy(),
             lse.cpu().numpy())
@@ -115,3 +135,27 @@ def test_step_is_deterministic_run_to_run(splits):
         again = run(batch, t, wl, False, splits)
         for a, b in zip(first, again):
             assert np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+@pytest.mark.parametrize("H", [16, 128])
+def test_fp8_latent_rows_are_batch_invariant_with_one_split(H):
+    """The same invariance over the fp8 latent cache (written on the GPU from
+    the bf16 rows), checked against the oracle over the dequantised rows."""
+    wl = synth.make_workload([5000, 700, 2048, 9000, 64], [1, 2, 1, 2, 1], H, seed=33, spare_pages=5)
+    kv8 = kv8_cache(wl)
+    B = wl.num_seqs
+    full_batch, full_t, _ = sub_workload(wl, list(range(B)), kv8=kv8)
+    full = run(full_batch, full_t, wl, False, 1)
+    o_ref, l_ref = oracle.sparse_mla(wl.q_mla.view(torch.int16).numpy(), kv8.numpy(), wl.block_table.numpy(),
+                                  wl.seq_lens.numpy(), wl.query_start.numpy(), full[1], wl.softmax_scale,
+                                  num_pages=wl.num_pages, kv_format="fp8")
+    check_mla(torch.from_numpy(full[2]).view(torch.bfloat16), torch.from_numpy(full[3]), o_ref, l_ref,
+              f"fp8 H={H} batch sparse MLA")
+    for li, seqs in enumerate([[b] for b in range(B)] + [list(reversed(range(B)))]):
+        batch, t, rows = sub_workload(wl, seqs, perm_seed=200 + li, kv8=kv8)
+        got = run(batch, t, wl, False, 1)
+        for o, r in enumerate(rows):
+            what = f"fp8 H={H}: row {r} with sequences {seqs}"
+            assert np.array_equal(got[1][o], full[1][r]), f"{what}: top-k"
+            assert np.array_equal(got[2][o], full[2][r]), f"{what}: out"
+            assert np.array_equal(got[3][o].view(np.uint32), full[3][r].view(np.uint32)), f"{what}: lse"
