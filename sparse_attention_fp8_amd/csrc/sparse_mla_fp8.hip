@@ -72,8 +72,12 @@ __device__ __forceinline__ v8bf fp8x8_to_v8bf(uint32_t w0, uint32_t w1) {
   return as_v8bf(u);
 }
 
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+// The packed pair is read back whole: element-wise reads of a bf16 vector
+// have given wrong lanes with this compiler.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+  const v2bf16 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 constexpr int kMaxTiles8 = DSA_MAX_TOPK / kTile8;   // 32 tiles per split at most
