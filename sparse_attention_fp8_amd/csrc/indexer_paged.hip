@@ -12,17 +12,19 @@
 // instructions per row and page.  The e4m3 decode happens inside the MFMA.
 // Accumulator layout: lane l holds token 16*nt + (l & 15) and heads
 // 16*mt + 4*(l >> 4) + i, so the weighted ReLU head sum is 16 in-lane FMAs
-// followed by a 3-shuffle reduce-scatter that leaves token l of the page in
-// lane l -- one coalesced 256-byte store per row and page.
+// (ReLU as one v_med3_f32) followed by a reduce-scatter of two VALU lane
+// swaps (v_permlane32_swap, v_permlane16_swap) that leaves token l of the page
+// in lane l -- one coalesced 256-byte store per row and page.
 //
 // Work balance: the pages of all sequences form one list; every workgroup
 // rebuilds its prefix sum in LDS and each wave takes an equal contiguous run
 // of it (so the grid depends only on host hints and no wave sits idle on
 // a short sequence).  A wave looks up the physical ids of up to 64 pages of
 // its run with one lane-parallel block-table load, and keeps the K tiles of
-// its next three pages in flight in a register ring while it multiplies the
-// current one.  HBM traffic per page: 8 KB codes + 256 B scales, read once,
-// coalesced 16-byte loads.
+// its next pages in flight in a register ring while it multiplies the current
+// one (two pages for one query row per sequence, one for two rows, which keeps
+// two waves per SIMD).  HBM traffic per page: 8 KB codes + 256 B scales, read
+// once, coalesced 16-byte loads.
 #include "common.h"
 #include "kernels.h"
 

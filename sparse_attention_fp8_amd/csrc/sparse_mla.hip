@@ -21,10 +21,12 @@
 //    from HBM straight into LDS with global_load_lds_dwordx4, double-buffered:
 //    tile i+1 is in flight while tile i is multiplied.  Each lane supplies its
 //    own source address, so the gather through the block table costs nothing
-//    extra; masked slots read a static zero row.  Rows are padded to 73
-//    sixteen-byte chunks (1168 B): an odd chunk count puts the 16 token rows an
-//    MFMA operand read touches on distinct LDS banks, and every operand address
-//    stays "lane base + immediate".
+//    extra; masked slots read a static zero row.  The LDS tile is made of 1 KB
+//    blocks (128-byte column group of the row, group of 8 rows) whose 16-byte
+//    slot s of row r8 holds the row's chunk s ^ r8: one wave-wide copy fills
+//    one block from eight whole 128-byte lines, and the operand reads spread
+//    over the banks.  The V^T operand of PV comes from transposing 16-bit LDS
+//    reads (ds_read_b64_tr_b16).
 //  * Row pointers are prepared two tiles ahead by wave 0 (index load one tile
 //    earlier than the block-table load), so no dependent global round trip
 //    sits on the critical path of a tile.

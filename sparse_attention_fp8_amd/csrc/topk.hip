@@ -31,7 +31,9 @@
 //    candidates.  Every member of the row's top-k is in its own chunk's top-k
 //    (fewer than k entries precede it in the row, hence in the chunk), so one
 //    more selection over the concatenated candidates -- already in index
-//    order -- is exact (the chunked exact top-k argument of the pages).
+//    order -- is exact (the chunked exact top-k argument of the pages).  Past
+//    four chunks the candidates of each group of four chunks are first reduced
+//    to their top k, in parallel, by the same argument one level up.
 #include <type_traits>
 
 #include "common.h"
