@@ -75,6 +75,34 @@ __device__ __forceinline__ int row_extent(const BatchArgs& a, int b, int r) {
   return e < 0 ? 0 : (e > L ? L : e);
 }
 
+// Sequence b of row r and its causal extent e_r (b = -1, e = 0 when no
+// sequence holds the row), for a full wave calling with the same r.  With at
+// most 63 sequences one round of lane-parallel loads gives both: lane j reads
+// query_start[j] and seq_lens[j], and b's entries are picked out by shuffles.
+// More sequences take the two-round search, then the extent loads.
+__device__ __forceinline__ void seq_and_extent_wave(const BatchArgs& a, int r, int& b, int& e) {
+  const int B = a.num_seqs;
+  if (B > 63) {
+    b = seq_of_row_wave(a.query_start, B, r);
+    e = b >= 0 ? row_extent(a, b, r) : 0;
+    return;
+  }
+  b = -1;
+  e = 0;
+  if (B <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int qv = lane <= B ? a.query_start[lane] : 0x7FFFFFFF;
+  const int lv = lane < B ? a.seq_lens[lane] : 0;
+  const int n1 = __popcll(__ballot(lane < B && qv <= r));
+  const int last = __shfl(qv, B, 64);
+  if (n1 == 0 || r >= last) return;
+  b = n1 - 1;
+  const int q0 = __shfl(qv, b, 64), q1 = __shfl(qv, b + 1, 64);
+  const int L = clamp_len(__shfl(lv, b, 64), a.max_seq_len);
+  const int x = L - (q1 - q0) + (r - q0) + 1;
+  e = x < 0 ? 0 : (x > L ? L : x);
+}
+
 // Order-preserving map float -> uint32 (larger float -> larger key), with -0
 // folded onto +0 so the two compare equal.
 __device__ __forceinline__ uint32_t float_key(float x) {

@@ -59,6 +59,22 @@ __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
 }
 
+// 4 bytes per lane from global memory into LDS at lds + 4 * lane, with the same
+// explicit-wait contract.
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt that waits until at most N vector-memory loads of this wave are
+// outstanding (N < 64), leaving the LDS and export counters alone.  Followed by
+// a compiler barrier so no LDS read of copied data is hoisted above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
 // N-way merge of the split partials: one wave per (row, head), 8 dims per lane.
 // Every load goes out before any is used -- the split maxima and sums
 // (lane-parallel, lane i <-> split i) and the accumulators of the first U

@@ -18,18 +18,26 @@
 //    probabilities are exchanged through LDS between the waves of that head
 //    tile, and every wave accumulates its own dims over all 64 tokens.
 //  * Gather: the 64 selected latent rows of a tile (64 x 1152 B) are copied
-//    from HBM straight into LDS with global_load_lds_dwordx4, double-buffered:
-//    tile i+1 is in flight while tile i is multiplied.  Each lane supplies its
-//    own source address, so the gather through the block table costs nothing
-//    extra; masked slots read a static zero row.  The LDS tile is made of 1 KB
-//    blocks (128-byte column group of the row, group of 8 rows) whose 16-byte
-//    slot s of row r8 holds the row's chunk s ^ r8: one wave-wide copy fills
-//    one block from eight whole 128-byte lines, and the operand reads spread
-//    over the banks.  The V^T operand of PV comes from transposing 16-bit LDS
-//    reads (ds_read_b64_tr_b16).
-//  * Row pointers are prepared two tiles ahead by wave 0 (index load one tile
-//    earlier than the block-table load), so no dependent global round trip
-//    sits on the critical path of a tile.
+//    from HBM straight into LDS with global_load_lds_dwordx4 into two buffers.
+//    With 16 heads the copy of tile i+2 is issued as soon as tile i's buffer
+//    is released, so two tiles are in flight whenever a wave waits (a wait
+//    with one tile in flight leaves the HBM queue half empty: a c2-sized
+//    gather takes about 1.6x as long).  Larger head blocks keep one tile
+//    ahead and spread its copy over the QK steps of the tile being
+//    multiplied, which hides the copy issue behind their MFMAs.  Each lane
+//    supplies its own source address, so the gather through the block table
+//    costs nothing extra; masked slots read a static
+//    zero row.  The LDS tile is made of 1 KB blocks (128-byte column group of
+//    the row, group of 8 rows) whose 16-byte slot s of row r8 holds the row's
+//    chunk s ^ r8: one wave-wide copy fills one block from eight whole
+//    128-byte lines, and the operand reads spread over the banks.  The V^T
+//    operand of PV comes from transposing 16-bit LDS reads
+//    (ds_read_b64_tr_b16).
+//  * Row pointers: wave 0 copies each tile's indices and then their
+//    block-table entries into a 4-slot LDS ring with direct global->LDS
+//    copies, three and two tiles ahead of use.  No register is ever written
+//    by a pending load, so every wait is an exact count of outstanding copies
+//    and none waits for a gather issued after the copy it needs.
 //  * QK: S^T[token, head] = C . Q^T with v_mfma_f32_16x16x32_bf16 (M = 16
 //    tokens, N = 16 heads, K = 32 dims, 18 steps over 576 dims); Q stays in
 //    registers.  The S^T accumulator gives each lane one head and 4 tokens of
@@ -58,21 +66,30 @@ __device__ __attribute__((aligned(16))) uint4 g_zero_row[kChunks] = {};
 template <int HT, int TP>
 struct MlaShared {
   unsigned char tile[2][kTileBytes];                 // double-buffered gathered rows
-  const unsigned char* rowptr[2][kTile];             // source row of each slot
-  uint64_t mask[2];                                   // valid slots of each buffer
+  int idx[4][kTile];                                  // indices of tile t (ring slot t % 4)
+  int page[4][kTile];                                 // their block-table entries
   uint2 p[HT][4][4][16];                             // bf16 probabilities [tile][g][head]
   float tmax[HT][TP][16];                             // per-part tile maxima
 };
 
-template <int HT, int TP>
+// DEEP: two tiles in flight while a wave waits (tile t + 2's copy goes out in
+// one burst when tile t's buffer is released).  Otherwise one tile ahead, its
+// copy spread over the QK steps of the tile being multiplied: with 64 heads a
+// tile carries enough MFMA work that a burst of copies stalls the waves longer
+// than the second tile in flight saves (measured: 64 heads over 128 rows,
+// 87.6 us one ahead against 96.8 us two ahead; 32 heads over 32 rows, 31.8
+// against 33.6 us; 16 heads over the same rows, 27.0 against 25.8 us).
+template <int HT, int TP, bool DEEP>
 __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   constexpr int NW = HT * TP;          // waves
   constexpr int TPT = 4 / TP;          // token tiles of 16 scored per wave
   constexpr int DW = kVDim / TP;       // output dims per wave
   constexpr int NDT = DW / 16;         // dim tiles per wave
   constexpr int RGW = kRowGroups / NW; // row groups each wave gathers
+  constexpr int ND = RGW * kChunkGroups;   // gather loads per wave and tile
   static_assert(RGW * NW == kRowGroups, "waves must split the row groups evenly");
   static_assert(DW % 128 == 0, "PV swizzle terms assume 128-dim aligned parts");
+  static_assert(ND + 2 < 64, "vmcnt range");
   __shared__ MlaShared<HT, TP> sh;
 
   const int R = a.batch.num_rows;
@@ -97,65 +114,63 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   const int slot1 = min(slot0 + a.split_slots, a.k);
   const int ntiles = (slot1 - slot0 + kTile - 1) / kTile;
 
-  // Row pointer of slot j (wave 0 only): index -> block table -> page row.
+  // Row pointers.  Wave 0 copies the indices of tile t (lane = token) into
+  // ring slot t % 4 of sh.idx, and later their block-table entries into
+  // sh.page, both with direct global->LDS copies: the chain then needs no
+  // register that a pending load writes, and every wait below is an exact
+  // count of this wave's outstanding copies.  Positions past the split are
+  // clamped to its last entry (and masked by position); an index outside
+  // [0, max_seq_len) reads table entry 0 of the row (and is masked by value).
   const int32_t* idx_row = a.indices + (int64_t)r * a.k;
-  auto load_idx = [&](int t) -> int {
-    const int j = slot0 + t * kTile + lane;
-    return (t < ntiles && j < slot1) ? idx_row[j] : -1;
+  int bc = 0, e = 0;
+  auto issue_idx = [&](int t) {
+    const int j = min(slot0 + t * kTile + lane, slot1 - 1);
+    lds_dma4(idx_row + j, lds_addr(sh.idx[t & 3]));
   };
-  int b = -1, e = 0;
-  // The block-table load needs only idx < max_seq_len to stay inside the row;
-  // the causal extent e and the page range are checked when the pointer is
-  // published, so the wait for that load comes as late as possible.
-  auto load_page = [&](int idx) -> int {
-    return (b >= 0 && idx >= 0 && idx < a.batch.max_seq_len)
-               ? a.batch.block_table[(int64_t)b * a.batch.bt_stride + (idx >> 6)] : -1;
+  auto issue_page = [&](int t) {
+    const int idx = sh.idx[t & 3][lane];
+    const int ic = (idx >= 0 && idx < a.batch.max_seq_len) ? idx : 0;
+    lds_dma4(a.batch.block_table + (int64_t)bc * a.batch.bt_stride + (ic >> 6), lds_addr(sh.page[t & 3]));
   };
-  auto publish = [&](int t, int idx, int page) {
-    const bool valid = idx >= 0 && idx < e && page >= 0 && page < a.batch.num_pages;
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(g_zero_row);
-    if (valid) src = reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page * a.kv_stride + (idx & 63) * kKvDim);
-    sh.rowptr[t & 1][lane] = src;
-    const uint64_t m = __ballot(valid);
-    if (lane == 0) sh.mask[t & 1] = t < ntiles ? m : 0ull;
+  // Source row of token tok of tile t; the static zero row when the token is
+  // padding, past the split, outside [0, e_r) or on a page outside the cache.
+  auto row_src = [&](int t, int tok, bool& valid) -> const unsigned char* {
+    const int idx = sh.idx[t & 3][tok];
+    const int page = sh.page[t & 3][tok];
+    valid = slot0 + t * kTile + tok < slot1 && idx >= 0 && idx < e && page >= 0 && page < a.batch.num_pages;
+    return valid ? reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page * a.kv_stride + (idx & 63) * kKvDim)
+                 : reinterpret_cast<const unsigned char*>(g_zero_row);
   };
   // Gather of tile t into buffer t & 1.  LDS layout of a tile: 1 KB block
   // (cg, rg) = (128-B column group of the row, group of 8 rows) at
   // (8 cg + rg) KB; inside it row r8 takes 128 B whose 16-B slot s holds the
   // row's chunk s ^ r8.  One wave-wide load fills one block: lane l copies
   // slot l & 7 of row l >> 3, so each load reads eight whole 128-B lines and
-  // each lane needs one row pointer per row group.
-  constexpr int ND = RGW * kChunkGroups;   // gather loads per wave and tile
-  auto gather_src = [&](int t, int j) -> const unsigned char* {
-    return sh.rowptr[t & 1][(wave * RGW + j) * 8 + (lane >> 3)] + (((lane & 7) ^ (lane >> 3)) << 4);
-  };
-  auto gather_one = [&](const unsigned char* const* src, uint32_t dst, int i) {
-    const int j = i / kChunkGroups, cg = i % kChunkGroups;
-    lds_dma16(src[j] + cg * 128, dst + (cg * kRowGroups + wave * RGW + j) * 1024);
-  };
-  auto gather = [&](int t) {
+  // each lane needs one row pointer per row group.  Masked rows read the zero
+  // row, so every wave issues exactly ND loads per tile.
+  auto gather = [&](int t) __attribute__((always_inline)) {
     const unsigned char* src[RGW];
 #pragma unroll
-    for (int j = 0; j < RGW; ++j) src[j] = gather_src(t, j);
+    for (int j = 0; j < RGW; ++j) {
+      bool v;
+      src[j] = row_src(t, (wave * RGW + j) * 8 + (lane >> 3), v) + (((lane & 7) ^ (lane >> 3)) << 4);
+    }
     const uint32_t dst = lds_addr(sh.tile[t & 1]);
 #pragma unroll
-    for (int i = 0; i < ND; ++i) gather_one(src, dst, i);
+    for (int i = 0; i < ND; ++i) {
+      const int j = i / kChunkGroups, cg = i % kChunkGroups;
+      lds_dma16(src[j] + cg * 128, dst + (cg * kRowGroups + wave * RGW + j) * 1024);
+    }
   };
 
-  // Prologue.  Vector loads retire in issue order, so wave 0's chain (indices
-  // with the sequence search, then the block table) goes out before any Q
-  // load: waiting for a link of the chain never waits for Q.
-  int idx_next = -1;   // indices of tile t + 2 (wave 0)
-  if (wave == 0) {
-    const int i0 = load_idx(0), i1 = load_idx(1);
-    idx_next = load_idx(2);
-    b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
-    e = b >= 0 ? row_extent(a.batch, b, r) : 0;
-    const int p0 = load_page(i0), p1 = load_page(i1);
-    publish(0, i0, p0);
-    publish(1, i1, p1);
+  // Prologue: wave 0's index copies of tiles 0..3 go out first, then Q (all
+  // waves), then the sequence search; the block-table copies of tiles 0..2
+  // follow once the indices are in.  Everything is waited for before the
+  // first gather, so inside the loop only copies are ever outstanding.
+  if (wave == 0 && ntiles > 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) issue_idx(t);
   }
-  asm volatile("" ::: "memory");
   // Q^T operand: lane supplies head h, dims 32*ks + 8*g .. +8.
   uint4 qreg[18];
   {
@@ -163,8 +178,20 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
   }
+  {
+    int b;
+    seq_and_extent_wave(a.batch, r, b, e);
+    bc = b >= 0 ? b : 0;
+  }
+  wait_vmcnt<0>();
+  if (wave == 0 && ntiles > 0) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) issue_page(t);
+    wait_vmcnt<0>();
+  }
   __syncthreads();
-  if (sh.mask[0] != 0ull) gather(0);
+  if (ntiles > 0) gather(0);
+  if (DEEP && ntiles > 1) gather(1);
 
   // Operand addresses (bytes into a tile).  QK: lane reads row tt*16 + n16,
   // chunk 4 ks + g; the swizzle term is x0 for even ks and x0 ^ 64 for odd.
@@ -186,32 +213,47 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   float m_run = kMaskSentinel;   // running max of the log2-domain scores of head h
   float l_part = 0.f;            // this lane's share of the running sum
 
+  // DEEP pipeline: the copy of tile t + 2 goes out as soon as every wave is
+  // done with tile t's buffer, and wave 0 issues the table copy of tile t + 3
+  // and the index copy of tile t + 4 just before it (copies retire in issue
+  // order, so waiting for those never waits for a gather issued after them).
+  // Otherwise: everything issued is waited for at the top of tile t, then wave
+  // 0 issues the table copy of tile t + 2 and the index copy of tile t + 3, and
+  // tile t + 1's copy is spread over tile t's QK steps.
   for (int t = 0; t < ntiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();                                   // tile t landed; rowptr(t+1) ready
-    const uint64_t mask = sh.mask[t & 1];
-    // Wave 0 starts the row pointers of tile t + 2: the block-table load goes
-    // out before the gather of tile t + 1, so waiting for it at publish() does
-    // not wait for the gather (vector loads retire in issue order).
-    int idx_cur = -1, page_cur = -1;
-    if (wave == 0) {
-      idx_cur = idx_next;
-      page_cur = load_page(idx_cur);
+    // this wave's copies of tile t: what was issued after them may stay out
+    if (!DEEP || t + 1 >= ntiles) wait_vmcnt<0>();
+    else if (wave == 0 && t >= 1 && t + 2 < ntiles) wait_vmcnt<ND + 2>();
+    else wait_vmcnt<ND>();
+    __syncthreads();                                   // tile t landed in every wave
+    uint64_t mask;
+    {
+      bool v;
+      row_src(t, lane, v);
+      mask = __ballot(v);
     }
-    if (wave == 0) idx_next = load_idx(t + 3);
-    // The gather of tile t + 1 is spread over this tile's QK steps: issued in
-    // one burst, its loads would stall the wave on the memory pipeline's
-    // backpressure before any compute of tile t starts.
-    const bool pre = t + 1 < ntiles && sh.mask[(t + 1) & 1] != 0ull;
+    // one-ahead schedule: sources of tile t + 1 (its table copy landed above)
+    const bool pre = !DEEP && t + 1 < ntiles;
     const unsigned char* gsrc[RGW];
     const uint32_t gdst = lds_addr(sh.tile[(t + 1) & 1]);
     if (pre) {
 #pragma unroll
-      for (int j = 0; j < RGW; ++j) gsrc[j] = gather_src(t + 1, j);
+      for (int j = 0; j < RGW; ++j) {
+        bool v;
+        gsrc[j] = row_src(t + 1, (wave * RGW + j) * 8 + (lane >> 3), v) + (((lane & 7) ^ (lane >> 3)) << 4);
+      }
     }
+    if (!DEEP && wave == 0 && t >= 1 && t + 2 < ntiles) {
+      issue_page(t + 2);
+      issue_idx(t + 3);
+    }
+    auto gather_one = [&](int i) {
+      const int j = i / kChunkGroups, cg = i % kChunkGroups;
+      lds_dma16(gsrc[j] + cg * 128, gdst + (cg * kRowGroups + wave * RGW + j) * 1024);
+    };
     if (pre && mask == 0ull) {
 #pragma unroll
-      for (int i = 0; i < ND; ++i) gather_one(gsrc, gdst, i);
+      for (int i = 0; i < ND; ++i) gather_one(i);
     }
 
     if (mask != 0ull) {
@@ -228,7 +270,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
           const int q = u * 18 + ks;
 #pragma unroll
           for (int i = 0; i < ND; ++i)
-            if (i * NQ / ND == q && pre) gather_one(gsrc, gdst, i);
+            if (i * NQ / ND == q && pre) gather_one(i);
           const unsigned char* cb = tile + ((ks & 1) ? qk1 : qk0) + (ks >> 1) * (kRowGroups * 1024) + tt * 2048;
           const uint4 cv = *reinterpret_cast<const uint4*>(cb);
           s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(cv), as_v8bf(qreg[ks]), s[u], 0, 0, 0);
@@ -300,9 +342,16 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
         }
       }
     }
-    // the tile's masks and row pointers of buffer t & 1 are no longer read:
-    // wave 0 publishes tile t + 2 there
-    if (wave == 0) publish(t + 2, idx_cur, page_cur);
+
+    if (DEEP && t + 2 < ntiles) {
+      if (wave == 0) wait_vmcnt<ND>();                 // table copy of tile t + 2, index copy of t + 3
+      __syncthreads();                                 // buffer t & 1 is free; tile t + 2's table visible
+      if (wave == 0 && t + 3 < ntiles) {
+        issue_page(t + 3);
+        issue_idx(t + 4);
+      }
+      gather(t + 2);
+    }
   }
 
   // l of head h over all tokens: lane groups, then the parts of the head tile
@@ -402,11 +451,11 @@ hipError_t launch_sparse_mla(const BatchArgs& batch, const uint16_t* q, int H, c
   const int64_t units = (int64_t)batch.num_rows * p.splits;
   const int64_t grid = (units + 7) / 8 * 8 * p.head_blocks;
   if (H == 16) {
-    hipLaunchKernelGGL((sparse_mla_kernel<1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<1, 4, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else if (H == 32) {
-    hipLaunchKernelGGL((sparse_mla_kernel<2, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<2, 2, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((sparse_mla_kernel<4, 2>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<4, 2, false>), dim3((unsigned)grid), dim3(512), 0, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;

@@ -99,14 +99,6 @@ struct MlaShared8 {
   float tmax[HT][TP][16];                                     // per-part tile maxima
 };
 
-// s_waitcnt that waits until at most n vector-memory loads of this wave are
-// outstanding (n < 64), leaving the LDS and export counters alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Byte offset inside a tile of the 16-byte slot `slot` of token `tok`, column
 // group `cg`.
 __device__ __forceinline__ int tile_off(int cg, int tok, int slot) {

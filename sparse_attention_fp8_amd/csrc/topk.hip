@@ -19,9 +19,8 @@
 //    key into 8 interleaved copies of a 2048-bin LDS histogram (lane l adds
 //    to copy l % 8), which spreads the atomics of the few hot bins; a block
 //    scan over the bins from the top finds the threshold bin.  A pass stops
-//    the search when the threshold bin is taken whole.  The keys of the
-//    threshold bin (usually a few percent) are compacted into an LDS list and
-//    passes two and three run over that list.
+//    the search when the threshold bin is taken whole.  Passes two and three
+//    rescan the registers, counting only keys that match the prefix so far.
 //  * Emission: each thread forms bit masks of its keys above the threshold
 //    and equal to it; one block scan gives every thread its output offset and
 //    tie budget; each thread walks the set bits of its mask, so it writes
@@ -50,7 +49,6 @@ constexpr int kMergeMax = 65536;       // candidates per row in the merge pass
 constexpr int kGroupChunks = 4;        // chunks one group merge reduces to k candidates
 constexpr int kBins = 2048;
 constexpr int kCopies = 8;             // interleaved copies of the pass-one histogram
-constexpr int kCand = 4096;            // LDS list for the threshold bin's keys
 
 struct TopkArgs {
   BatchArgs batch;
@@ -74,7 +72,6 @@ struct TopkArgs {
 struct Shared {
   int hist1[kBins * kCopies];
   int hist2[kBins];
-  uint32_t cand[kCand];
   int out[DSA_MAX_TOPK];
   int wave_tot[kWaves];
   int misc[4];
@@ -235,16 +232,17 @@ __device__ __forceinline__ void find_digit(const int* hist, int rem, Shared& sh)
 // threshold below is at least 2^21 - 1 (the threshold bin holds a valid key),
 // so the later comparisons exclude key 0 by themselves.
 //  pass 1: 11-bit top digit of every key;
-//  then the keys of the threshold bin are compacted into an LDS list and
-//  passes 2 and 3 (11 and 10 bits) run over that list; if the bin is too
-//  large for the list, passes 2 and 3 scan the registers.
+//  passes 2 and 3 (11 and 10 bits) scan the registers again and count only
+//  the keys whose higher digits match the prefix found so far.  (Compacting
+//  the threshold bin into an LDS list first costs more than it saves: its
+//  per-key mask build and predicated stores take as long as both scans.)
 template <int KPT>
 __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   const int l = lane_id();
   for (int i = threadIdx.x; i < kBins * kCopies / 4; i += kThreads)
     reinterpret_cast<int4*>(sh.hist1)[i] = make_int4(0, 0, 0, 0);
   for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist2[i] = 0;
-  if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; sh.misc[3] = 0; }
+  if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; }
   __syncthreads();
   const int copy = l & (kCopies - 1);
 #pragma unroll
@@ -265,43 +263,6 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   constexpr int widths[2] = {11, 10};
   uint32_t mask = 0xFFE00000u;
   int* const hists[2] = {sh.hist2, sh.hist1};
-  if (in_bin <= kCand) {
-    // compact the bin's keys: one LDS atomic per wave reserves the slots
-    MaskT<KPT> mb = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      mb |= (MaskT<KPT>)((keys.v[j] & mask) == prefix) << j;
-    const int mine = popc(mb);
-    const int incl = wave_scan_dpp(mine);
-    int base = 0;
-    if (l == 63 && incl > 0) base = atomicAdd(&sh.misc[3], incl);
-    base = __builtin_amdgcn_readlane(base, 63) + incl - mine;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if ((mb >> j) & 1) {
-        sh.cand[base] = keys.v[j];
-        ++base;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      int* hist = hists[pass];
-      const uint32_t dmask = (1u << widths[pass]) - 1u;
-      for (int i = threadIdx.x; i < in_bin; i += kThreads) {
-        const uint32_t key = sh.cand[i];
-        if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shifts[pass]) & dmask)], 1);
-      }
-      __syncthreads();
-      find_digit<1>(hist, rem, sh);
-      rem -= sh.misc[1];
-      prefix |= (uint32_t)sh.misc[0] << shifts[pass];
-      mask |= dmask << shifts[pass];
-      if (rem == sh.misc[2]) return Selection{prefix - 1u, 0};
-    }
-    return Selection{prefix, rem};
-  }
-  // large threshold bin: passes 2 and 3 over the registers
   __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -368,8 +329,8 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
   Shared& sh = lds.s;
   const int r = blockIdx.x / a.nchunks;
   const int c = blockIdx.x % a.nchunks;
-  const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
-  const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
+  int b, e;
+  seq_and_extent_wave(a.batch, r, b, e);
   const int k = a.k;
   const float* row = a.logits + (int64_t)r * a.logits_stride;
   Keys<KPT> keys;
@@ -429,8 +390,8 @@ __global__ void __launch_bounds__(kThreads) topk_group_kernel(TopkArgs a) {
   __shared__ Shared sh;
   const int r = blockIdx.x / a.ngroups;
   const int g = blockIdx.x % a.ngroups;
-  const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
-  const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
+  int b, e;
+  seq_and_extent_wave(a.batch, r, b, e);
   const int k = a.k;
   const int nch = (e + kChunk - 1) / kChunk;
   const int c0 = g * kGroupChunks;
@@ -471,8 +432,8 @@ template <int KPT>
 __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
   __shared__ Shared sh;
   const int r = blockIdx.x;
-  const int b = seq_of_row_wave(a.batch.query_start, a.batch.num_seqs, r);
-  const int e = b >= 0 ? row_extent(a.batch, b, r) : 0;
+  int b, e;
+  seq_and_extent_wave(a.batch, r, b, e);
   if (e <= kChunk) return;
   const int k = a.k;
   const int nch = (e + kChunk - 1) / kChunk;
