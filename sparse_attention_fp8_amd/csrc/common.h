@@ -173,4 +173,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// 32-bit LDS address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global->LDS copies: 16 (or 4) bytes per lane into LDS at
+// lds + 16 * lane (4 * lane), lds wave-uniform.  Written as inline asm so the
+// compiler does not treat a copy as an LDS store that every later LDS read
+// must wait for (that would drain the next tile's copy before the current one
+// is read).  The kernels wait for their copies themselves (vmcnt).
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+
+// s_waitcnt that waits until at most N vector-memory operations of this wave
+// are outstanding (N < 64), leaving the LDS and export counters alone.
+// Followed by a compiler barrier so no LDS read of copied data is hoisted
+// above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace dsa

@@ -7,24 +7,31 @@
 //
 // gfx950 design.  One wave owns one 64-token page at a time and computes the
 // whole [64 heads x 64 tokens] block of one or two query rows with the fp8
-// MFMA v_mfma_f32_16x16x128_f8f6f4 (M = 16 heads, N = 16 tokens, K = 128, the
-// full head dim in one instruction): 4 head tiles x 4 token tiles = 16
-// instructions per row and page.  The e4m3 decode happens inside the MFMA.
-// Accumulator layout: lane l holds token 16*nt + (l & 15) and heads
-// 16*mt + 4*(l >> 4) + i, so the weighted ReLU head sum is 16 in-lane FMAs
-// (ReLU as one v_med3_f32) followed by a reduce-scatter of two VALU lane
-// swaps (v_permlane32_swap, v_permlane16_swap) that leaves token l of the page
-// in lane l -- one coalesced 256-byte store per row and page.
+// MFMA v_mfma_f32_32x32x64_f8f6f4 (M = 32 heads, N = 32 tokens, K = 64; the
+// e4m3 decode happens inside the MFMA): 2 head tiles x 2 token steps x 2 K
+// halves = 8 instructions per row and page.  (The 16x16x128 shape needs
+// about 1.4x the issue time per product here, and that time was not hidden
+// behind the loads.)  C layout: lane l holds 16 heads of token l % 32, so the
+// weighted ReLU head sum is 32 in-lane FMAs (ReLU as one v_med3_f32) per
+// token step, and one v_permlane32_swap leaves token l of the page in lane l
+// -- one coalesced 256-byte store per row and page.
+//
+// Loads: each page (8 KB codes + 256 B scales) is copied whole into a per-wave
+// LDS ring with global_load_lds_dwordx4, eight whole 128-byte key rows per
+// instruction; key row n's 16-byte chunk c sits in slot c ^ ((n >> 1) & 7),
+// so the B-operand reads (16 consecutive keys, one chunk) hit distinct
+// banks.  Reading the operands straight from HBM in the MFMA layout touches
+// 32 half-used lines per instruction and measured about 30 % slower.  Two
+// pages per wave are in flight: the next copy into a slot goes out as soon
+// as the page in it is read into registers.  The ring is wave-private, so no
+// barrier follows the prefix build.
 //
 // Work balance: the pages of all sequences form one list; every workgroup
-// rebuilds its prefix sum in LDS and each wave takes an equal contiguous run
-// of it (so the grid depends only on host hints and no wave sits idle on
-// a short sequence).  A wave looks up the physical ids of up to 64 pages of
-// its run with one lane-parallel block-table load, and keeps the K tiles of
-// its next pages in flight in a register ring while it multiplies the current
-// one (two pages for one query row per sequence, one for two rows, which keeps
-// two waves per SIMD).  HBM traffic per page: 8 KB codes + 256 B scales, read
-// once, coalesced 16-byte loads.
+// (8 waves, one per CU) rebuilds its prefix sum in LDS and each wave takes an
+// equal contiguous run of it (so the grid depends only on host hints and no
+// wave sits idle on a short sequence).  A wave looks up the physical ids of
+// up to 64 pages of its run with one lane-parallel block-table load; the q
+// rows of its first sequence are loaded with it.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,6 +50,22 @@ struct PagedArgs {
   int clean;
 };
 
+constexpr int kWavesPg = 8;                              // waves per workgroup, one workgroup per CU
+constexpr int kRingPg = 2;                               // pages in flight per wave (LDS ring)
+constexpr int kPageLds = kPage * kIdxDim + kPage * 4;    // 8448: codes, then the 64 scales
+constexpr int kCopiesPerPage = kPage * kIdxDim / 1024 + 1;   // 8 code copies + 1 scale copy
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int swz(int n) { return (n >> 1) & 7; }
+__device__ __attribute__((aligned(16))) uint8_t g_zero_page[kPageLds] = {};
+
+struct PagedShared {
+  unsigned char ring[kWavesPg][kRingPg][kPageLds];
+  int pref[DSA_MAX_SEQS + 1];
+  int wave_tot[kWavesPg];
+};
+
 // Pages to compute for sequence b: ceil(L_b / 64) if it has rows, else 0.
 __device__ __forceinline__ int seq_pages(const BatchArgs& a, int b) {
   const int q0 = a.query_start[b], q1 = a.query_start[b + 1];
@@ -50,58 +73,40 @@ __device__ __forceinline__ int seq_pages(const BatchArgs& a, int b) {
   return (clamp_len(a.seq_lens[b], a.max_seq_len) + kPage - 1) / kPage;
 }
 
-// s_pref[b] = sum of seq_pages over sequences before b; s_pref[B] = total.
-__device__ void build_page_prefix(const BatchArgs& a, int* s_pref, int* s_wave) {
+// pref[b] = sum of seq_pages over sequences before b; pref[B] = total.
+__device__ void build_page_prefix(const BatchArgs& a, int* pref, int* wave_tot) {
   const int B = a.num_seqs;
   const int per = (B + blockDim.x - 1) / blockDim.x;
   const int start = threadIdx.x * per;
   const int stop = min(start + per, B);
   int local = 0;
   for (int b = start; b < stop; ++b) local += seq_pages(a, b);
-  int incl = wave_inclusive_scan(local);
+  const int incl = wave_inclusive_scan(local);
   const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  if (lane_id() == 63) s_wave[wave] = incl;
+  if (lane_id() == 63) wave_tot[wave] = incl;
   __syncthreads();
   int before = 0, total = 0;
   for (int i = 0; i < nwaves; ++i) {
-    if (i < wave) before += s_wave[i];
-    total += s_wave[i];
+    if (i < wave) before += wave_tot[i];
+    total += wave_tot[i];
   }
   int run = before + incl - local;
   for (int b = start; b < stop; ++b) {
-    s_pref[b] = run;
+    pref[b] = run;
     run += seq_pages(a, b);
   }
-  if (threadIdx.x == 0) s_pref[B] = total;
+  if (threadIdx.x == 0) pref[B] = total;
   __syncthreads();
 }
 
-// Largest b with s_pref[b] <= p (p < total).
-__device__ __forceinline__ int find_seq(const int* s_pref, int B, int p) {
+// Largest b with pref[b] <= p (p < total).
+__device__ __forceinline__ int find_seq(const int* pref, int B, int p) {
   int lo = 0, hi = B;
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
-    if (s_pref[mid] <= p) lo = mid; else hi = mid;
+    if (pref[mid] <= p) lo = mid; else hi = mid;
   }
   return lo;
-}
-
-struct KTile {
-  v8i k[4];     // B operands of the 4 token tiles
-  float scale;  // kscale of token `lane` of the page
-};
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-
-// Streaming (non-temporal) load of 32 bytes: K pages are read exactly once.
-__device__ __forceinline__ v8i load_v8i(const uint8_t* p) {
-  const v4i* s = reinterpret_cast<const v4i*>(p);
-  const v4i x0 = __builtin_nontemporal_load(s);
-  const v4i x1 = __builtin_nontemporal_load(s + 1);
-  v8i r;
-  r[0] = x0[0]; r[1] = x0[1]; r[2] = x0[2]; r[3] = x0[3];
-  r[4] = x1[0]; r[5] = x1[1]; r[6] = x1[2]; r[7] = x1[3];
-  return r;
 }
 
 __device__ __forceinline__ v8i load_v8i_cached(const uint8_t* p) {
@@ -113,79 +118,76 @@ __device__ __forceinline__ v8i load_v8i_cached(const uint8_t* p) {
   return r;
 }
 
-__device__ __forceinline__ void load_ktile(KTile& t, const uint8_t* page, int lane) {
-  const int n = lane & 15, kg = lane >> 4;
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) t.k[nt] = load_v8i(page + (16 * nt + n) * kIdxDim + kg * 32);
-  t.scale = __builtin_nontemporal_load(reinterpret_cast<const float*>(page + kIdxScaleOff) + lane);
-}
-
 struct QRow {
-  v8i q[4];      // A operands of the 4 head tiles
-  v4f w[4];      // weights of this lane's 16 heads (4 per head tile)
+  v8i q[2][2];       // A operands: head tile mt (32 heads), K half kh
+  float w[2][16];    // weights of the 16 heads this lane holds per head tile
 };
 
+// A operand: lane l supplies head 32 mt + l % 32, code bytes 64 kh +
+// 32 (l / 32) .. +32.  C layout: item i of lane l is head 32 mt + (i % 4) +
+// 4 (l / 32) + 8 (i / 4) of token l % 32 (the layout the prefill kernel's
+// in-bounds lane probe checked), so the lane's weights are those heads'.
 __device__ __forceinline__ void load_qrow(QRow& t, const uint8_t* q, const float* w, int r, int lane) {
-  const int n = lane & 15, kg = lane >> 4;
+  const int hq = lane & 31, hk = lane >> 5;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    t.q[mt] = load_v8i_cached(q + ((size_t)r * kIdxHeads + 16 * mt + n) * kIdxDim + kg * 32);
-    const float4 ww = *reinterpret_cast<const float4*>(w + (size_t)r * kIdxHeads + 16 * mt + 4 * kg);
-    t.w[mt][0] = ww.x; t.w[mt][1] = ww.y; t.w[mt][2] = ww.z; t.w[mt][3] = ww.w;
+  for (int mt = 0; mt < 2; ++mt) {
+    const uint8_t* qp = q + ((size_t)r * kIdxHeads + 32 * mt + hq) * kIdxDim + 32 * hk;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) t.q[mt][kh] = load_v8i_cached(qp + 64 * kh);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 ww = *reinterpret_cast<const float4*>(w + (size_t)r * kIdxHeads + 32 * mt + 8 * g + 4 * hk);
+      t.w[mt][4 * g] = ww.x; t.w[mt][4 * g + 1] = ww.y; t.w[mt][4 * g + 2] = ww.z; t.w[mt][4 * g + 3] = ww.w;
+    }
   }
 }
 
-// sum_h w_h * relu(q_h . k_s) for token `lane` of the page (before the K scale).
-__device__ __forceinline__ float page_row_logit(const QRow& qr, const KTile& kt, int lane) {
-  // The four products of a token tile are issued before any is consumed (and
-  // the next tile's before this tile's epilogue), so no product waits alone
-  // for the MFMA latency.
-  float part[4];
-  v4f acc[2][4];
+// sum_h w_h * relu(q_h . k_s) for token `lane` of the page (before the K
+// scale).  b[ks][kh]: B operand of token step ks (32 tokens), K half kh.
+__device__ __forceinline__ float page_row_logit(const QRow& qr, const v8i (&b)[2][2]) {
+  // all eight products are issued before the first epilogue reads one
+  const v16f z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  v16f acc[2][2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-    acc[0][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qr.q[mt], kt.k[0], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                  0, 0, 0, 0, 0, 0);
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    if (nt + 1 < 4) {
+    for (int mt = 0; mt < 2; ++mt)
+      acc[ks][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qr.q[mt][0], b[ks][0], z, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        acc[(nt + 1) & 1][mt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            qr.q[mt], kt.k[nt + 1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-    }
-    float s = 0.f;
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
+      acc[ks][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qr.q[mt][1], b[ks][1], acc[ks][mt],
+                                                                    0, 0, 0, 0, 0, 0);
+  float part[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(qr.w[mt][i], relu_finite(acc[nt & 1][mt][i]), s);
-    part[nt] = s;
+  for (int ks = 0; ks < 2; ++ks) {
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p[i & 3] = fmaf(qr.w[mt][i], relu_finite(acc[ks][mt][i]), p[i & 3]);
+    part[ks] = (p[0] + p[1]) + (p[2] + p[3]);
   }
-  // Reduce-scatter over the 4 lane groups g = lane >> 4 (each holds 16 of the
-  // 64 heads of every token tile): afterwards lane l holds token tile g,
-  // column l & 15, i.e. page token l.
-  const int g = lane >> 4;
-  const bool hi = g >= 2;
-  float send0 = hi ? part[0] : part[2];
-  float send1 = hi ? part[1] : part[3];
-  float a0 = (hi ? part[2] : part[0]) + lane_xor32(send0);
-  float a1 = (hi ? part[3] : part[1]) + lane_xor32(send1);
-  const bool odd = g & 1;
-  float send = odd ? a0 : a1;
-  return (odd ? a1 : a0) + lane_xor16(send);
+  // Lane l holds half the heads of token l % 32 of both steps; one lane swap
+  // gives lanes 0-31 the other half of step 0 and lanes 32-63 the other half
+  // of step 1, so afterwards lane l holds page token l.
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
 template <int QL>
-__global__ void __launch_bounds__(256) indexer_paged_kernel(PagedArgs a) {
-  __shared__ int s_pref[DSA_MAX_SEQS + 1];
-  __shared__ int s_wave[4];
-  build_page_prefix(a.batch, s_pref, s_wave);
+__global__ void __launch_bounds__(64 * kWavesPg) indexer_paged_kernel(PagedArgs a) {
+  __shared__ PagedShared sh;
+  build_page_prefix(a.batch, sh.pref, sh.wave_tot);
+  const int* s_pref = sh.pref;
 
   const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int B = a.batch.num_seqs;
   const int total = s_pref[B];
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * kWavesPg;
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPg + wave;
   const int p_begin = (int)((int64_t)total * gw / nw);
   const int p_end = (int)((int64_t)total * (gw + 1) / nw);
   if (p_begin >= p_end) return;
@@ -206,42 +208,81 @@ __global__ void __launch_bounds__(256) indexer_paged_kernel(PagedArgs a) {
       lid = (id >= 0 && id < a.batch.num_pages) ? id : -1;
     }
   };
-  // K tiles of the next kRing pages stay in flight (a register ring); each
-  // slot keeps its page's id, sequence and page index, so reloading the page
-  // table for later pages never disturbs a pending slot.
-  constexpr int kRing = QL == 1 ? 2 : 1;
-  KTile kt[kRing];
-  int m_id[kRing], m_b[kRing], m_j[kRing];
-  auto issue = [&](int slot, int p) {
-    if (p < p_end) {
-      if (p - pb >= 64) load_batch(p);
-      m_id[slot] = __builtin_amdgcn_readlane(lid, p - pb);
-      m_b[slot] = __builtin_amdgcn_readlane(lb, p - pb);
-      m_j[slot] = __builtin_amdgcn_readlane(lj, p - pb);
-      if (m_id[slot] >= 0) load_ktile(kt[slot], a.cache + (int64_t)m_id[slot] * a.page_stride, lane);
+  // Copy of page p into ring slot (p - p_begin) % kRingPg: 8 copies of eight key
+  // rows each (lane l: row 8 i + l / 8, slot l % 8 holding chunk
+  // (l % 8) ^ swz(row)), then the 64 scales (lanes 0-15).  A page outside the
+  // cache copies a static zero page, so every page costs exactly
+  // kCopiesPerPage copies and the waits below count them exactly.
+  int m_id[kRingPg], m_b[kRingPg], m_j[kRingPg];
+  auto issue = [&](int p) {
+    if (p - pb >= 64) load_batch(p);
+    const int slot = (p - p_begin) % kRingPg;
+    m_id[slot] = __builtin_amdgcn_readlane(lid, p - pb);
+    m_b[slot] = __builtin_amdgcn_readlane(lb, p - pb);
+    m_j[slot] = __builtin_amdgcn_readlane(lj, p - pb);
+    const uint8_t* src = m_id[slot] >= 0 ? a.cache + (int64_t)m_id[slot] * a.page_stride : g_zero_page;
+    const uint32_t dst = lds_addr(sh.ring[wave][slot]);
+    const int rl = lane >> 3, sl = lane & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * i + rl;
+      lds_dma16(src + row * kIdxDim + 16 * (sl ^ swz(row)), dst + i * 1024);
     }
+    if (lane < 16) lds_dma16(src + kIdxScaleOff + 16 * lane, dst + kPage * kIdxDim);
   };
 
   QRow qr[QL];
   int cur_b = -1, row0 = 0, nrows = 0, L = 0, q_len = 0, q0 = 0;
-
-  auto compute = [&](int slot) {
-    const KTile& t = kt[slot];
-    const int id = m_id[slot], b = m_b[slot], j = m_j[slot];
-    if (b != cur_b) {
-      cur_b = b;
-      q0 = a.batch.query_start[b];
-      const int q1 = a.batch.query_start[b + 1];
-      q_len = q1 - q0;
-      row0 = max(q0, 0);
-      nrows = min(q1, a.batch.num_rows) - row0;
-      L = clamp_len(a.batch.seq_lens[b], a.batch.max_seq_len);
-      if (nrows <= QL) {
+  // Switch to sequence b; with at most QL rows their q and weights are loaded
+  // once here.
+  auto set_seq = [&](int b) {
+    cur_b = b;
+    q0 = a.batch.query_start[b];
+    const int q1 = a.batch.query_start[b + 1];
+    q_len = q1 - q0;
+    row0 = max(q0, 0);
+    nrows = min(q1, a.batch.num_rows) - row0;
+    L = clamp_len(a.batch.seq_lens[b], a.batch.max_seq_len);
+    if (nrows <= QL) {
 #pragma unroll
-        for (int jj = 0; jj < QL; ++jj)
-          if (jj < nrows) load_qrow(qr[jj], a.q, a.w, row0 + jj, lane);
-      }
+      for (int jj = 0; jj < QL; ++jj)
+        if (jj < nrows) load_qrow(qr[jj], a.q, a.w, row0 + jj, lane);
     }
+  };
+
+  // B-operand offsets inside a page: token 32 ks + l % 32, chunks
+  // 4 kh + 2 (l / 32) and the next one.
+  const int nb = lane & 31, hb = lane >> 5;
+  int boff[2][2][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = 32 * ks + nb;
+        boff[ks][kh][c] = row * kIdxDim + 16 * ((4 * kh + 2 * hb + c) ^ swz(row));
+      }
+
+  auto compute = [&](int p) {
+    const int slot = (p - p_begin) % kRingPg;
+    const int id = m_id[slot], b = m_b[slot], j = m_j[slot];
+    const unsigned char* tile = sh.ring[wave][slot];
+    v8i bop[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const v4i x0 = *reinterpret_cast<const v4i*>(tile + boff[ks][kh][0]);
+        const v4i x1 = *reinterpret_cast<const v4i*>(tile + boff[ks][kh][1]);
+        bop[ks][kh] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      }
+    const float scale = reinterpret_cast<const float*>(tile + kPage * kIdxDim)[lane];
+    // the slot is free once these reads have landed: page p + kRingPg goes there
+    wait_lgkmcnt0();
+    if (p + kRingPg < p_end) issue(p + kRingPg);
+    if (b != cur_b) set_seq(b);
+
     const int s = j * kPage + lane;  // logical token of this lane
     const bool in_stride = s < a.logits_stride;
     for (int g0 = 0; g0 < nrows; g0 += QL) {
@@ -256,7 +297,7 @@ __global__ void __launch_bounds__(256) indexer_paged_kernel(PagedArgs a) {
         const int r = row0 + g0 + jj;
         int e = L - q_len + (r - q0) + 1;
         e = e < 0 ? 0 : e;
-        const float v = id >= 0 ? page_row_logit(qr[jj], t, lane) * t.scale : -INFINITY;
+        const float v = id >= 0 ? page_row_logit(qr[jj], bop) * scale : -INFINITY;
         float* dst = a.logits + (int64_t)r * a.logits_stride + s;
         if (s < e) {
           if (in_stride) *dst = v;
@@ -268,16 +309,21 @@ __global__ void __launch_bounds__(256) indexer_paged_kernel(PagedArgs a) {
   };
 
   load_batch(p_begin);
+  // q of the first page's sequence goes out with the block-table load
+  set_seq(find_seq(s_pref, B, p_begin));
 #pragma unroll
-  for (int i = 0; i < kRing; ++i) issue(i, p_begin + i);
-  for (int p = p_begin; p < p_end; p += kRing) {
-#pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      if (p + i < p_end) {
-        compute(i);
-        issue(i, p + i + kRing);
-      }
-    }
+  for (int i = 0; i < kRingPg; ++i)
+    if (p_begin + i < p_end) issue(p_begin + i);
+  for (int p = p_begin; p < p_end; ++p) {
+    // this page's copies; what was issued after them (the next pages' copies,
+    // logit stores, any reload) may stay in flight
+    const int later = min(p_end - 1 - p, kRingPg - 1);
+    static_assert(kRingPg <= 4, "wait cases");
+    if (later >= 3) wait_vmcnt<3 * kCopiesPerPage>();
+    else if (later == 2) wait_vmcnt<2 * kCopiesPerPage>();
+    else if (later == 1) wait_vmcnt<kCopiesPerPage>();
+    else wait_vmcnt<0>();
+    compute(p);
   }
 }
 
@@ -309,16 +355,16 @@ hipError_t launch_indexer_paged(const BatchArgs& batch, const uint8_t* q, const 
                                 int64_t logits_stride, int clean, int num_cus, hipStream_t stream) {
   PagedArgs a{batch, q, w, cache, page_stride, logits, logits_stride, clean};
   const int64_t max_pages = (int64_t)batch.num_seqs * ((batch.max_seq_len + kPage - 1) / kPage);
-  // Two 4-wave workgroups per CU keep every SIMD busy; fewer when there is
-  // less than a page per wave.
-  int64_t grid = (max_pages + 3) / 4;
+  // One 8-wave workgroup per CU (its LDS ring takes most of the CU); fewer
+  // when there is less than a page per wave.
+  int64_t grid = (max_pages + kWavesPg - 1) / kWavesPg;
   grid = grid < 1 ? 1 : grid;
-  if (grid > 2 * (int64_t)num_cus) grid = 2 * (int64_t)num_cus;
+  if (grid > (int64_t)num_cus) grid = num_cus;
   if (batch.num_rows > 0 && batch.num_seqs > 0 && max_pages > 0) {
     if (batch.max_q_len <= 1) {
-      hipLaunchKernelGGL(indexer_paged_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(indexer_paged_kernel<1>, dim3((unsigned)grid), dim3(64 * kWavesPg), 0, stream, a);
     } else {
-      hipLaunchKernelGGL(indexer_paged_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(indexer_paged_kernel<2>, dim3((unsigned)grid), dim3(64 * kWavesPg), 0, stream, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

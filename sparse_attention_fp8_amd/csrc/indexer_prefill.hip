@@ -53,17 +53,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 // times the slot XORed with (n >> 1) & 7 does that.
 __device__ __forceinline__ int swz(int n) { return (n >> 1) & 7; }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds
-// wave-uniform).  Inline asm: the compiler would otherwise make every later
-// LDS read wait for the copy; the kernel waits (vmcnt) before its barrier.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
-}
-
 // Source of rows and scales of pages the chunk does not have.
 __device__ __attribute__((aligned(16))) uint32_t g_zero_kv[64] = {};
 

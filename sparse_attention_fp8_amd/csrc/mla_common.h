@@ -45,36 +45,6 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   return r;
 }
 
-// 32-bit LDS address of a pointer into a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (lds wave-uniform).  Written as inline asm so the compiler does not treat
-// the transfer as an LDS store that every later LDS read must wait for: it
-// would otherwise drain the gather of the next tile before reading the current
-// one.  The kernel waits for these loads itself (vmcnt) before its barrier.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
-}
-
-// 4 bytes per lane from global memory into LDS at lds + 4 * lane, with the same
-// explicit-wait contract.
-__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
-}
-
-// s_waitcnt that waits until at most N vector-memory loads of this wave are
-// outstanding (N < 64), leaving the LDS and export counters alone.  Followed by
-// a compiler barrier so no LDS read of copied data is hoisted above it.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
-
 // N-way merge of the split partials: one wave per (row, head), 8 dims per lane.
 // Every load goes out before any is used -- the split maxima and sums
 // (lane-parallel, lane i <-> split i) and the accumulators of the first U

@@ -102,17 +102,6 @@ __device__ __forceinline__ uint64_t drop_highest(uint64_t m) {
   return m & ~(0x8000000000000000ull >> __builtin_clzll(m));
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds
-// wave-uniform).  Inline asm: the compiler would otherwise treat the copy as an
-// LDS store that all later LDS reads wait for; the caller waits (vmcnt) itself.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
-}
-
 // Inclusive prefix sum over the 64 lanes: DPP shifts inside each row of 16
 // lanes, then the row totals are read out as scalars and added.
 __device__ __forceinline__ int wave_scan_dpp(int v) {
