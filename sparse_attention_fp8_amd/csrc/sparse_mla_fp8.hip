@@ -144,6 +144,20 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   const int ntiles = (slot1 - slot0 + kTile8 - 1) / kTile8;
 
   uint4 qreg[18];
+  // q operands.  Latent pair j (dims 64 j .. 64 j + 63): MFMA 2 j takes dims
+  // 64 j + 16 g + 0..7, MFMA 2 j + 1 dims 64 j + 16 g + 8..15 (the k order the
+  // 128-bit code reads deliver).  Rope step s: dims 512 + 32 s + 8 g + 0..7.
+  {
+    const uint16_t* qp = a.q + ((int64_t)r * a.H + h) * kKvDim;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qreg[2 * j] = *reinterpret_cast<const uint4*>(qp + 64 * j + 16 * g);
+      qreg[2 * j + 1] = *reinterpret_cast<const uint4*>(qp + 64 * j + 16 * g + 8);
+    }
+    qreg[16] = *reinterpret_cast<const uint4*>(qp + kVDim + 8 * g);
+    qreg[17] = *reinterpret_cast<const uint4*>(qp + kVDim + 32 + 8 * g);
+  }
+  asm volatile("" ::: "memory");   // q stays ahead of the prologue's loads, whose waits cover it
   // Prologue.  Every wave turns its tiles' indices into cache slots: tile t
   // belongs to wave t % NW, its entry lane to this lane.  All index loads go
   // out with the sequence search, then all block-table loads, so the chain is
@@ -216,29 +230,15 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
 #pragma unroll
     for (int i = 0; i < ND; ++i) gather_one(src, ssrc, dst, i);
   };
-  // Two tiles in flight pay off only once the pipeline runs for a while: with a
-  // few tiles per split, asking for two at once delays the first.
+  // Two tiles in flight pay off only once the pipeline runs for a while: with
+  // 4 tiles per split (c2) asking for two at once delays the first (24.9 us
+  // against 24.0 us).
   const int depth = (DEPTH > 1 && ntiles >= kDeepTiles) ? DEPTH : 1;
-  // Tile 0's copy goes out first, then q, which arrives while the copy is in
-  // flight; one wait then covers both, so inside the loop no load but the
-  // copies is ever outstanding and the waits there count copies only.
-  if (ntiles > 0) gather_all(0);
-  // q operands.  Latent pair j (dims 64 j .. 64 j + 63): MFMA 2 j takes dims
-  // 64 j + 16 g + 0..7, MFMA 2 j + 1 dims 64 j + 16 g + 8..15 (the k order the
-  // 128-bit code reads deliver).  Rope step s: dims 512 + 32 s + 8 g + 0..7.
-  {
-    const uint16_t* qp = a.q + ((int64_t)r * a.H + h) * kKvDim;
+  // q went out before the prologue's loads and the prologue waited for those,
+  // so inside the loop no load but the copies is ever outstanding and the
+  // waits there count copies only.
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qreg[2 * j] = *reinterpret_cast<const uint4*>(qp + 64 * j + 16 * g);
-      qreg[2 * j + 1] = *reinterpret_cast<const uint4*>(qp + 64 * j + 16 * g + 8);
-    }
-    qreg[16] = *reinterpret_cast<const uint4*>(qp + kVDim + 8 * g);
-    qreg[17] = *reinterpret_cast<const uint4*>(qp + kVDim + 32 + 8 * g);
-  }
-  wait_vmcnt<0>();
-#pragma unroll
-  for (int t = 1; t < DEPTH; ++t)
+  for (int t = 0; t < DEPTH; ++t)
     if (t < depth && t < ntiles) gather_all(t);
 
   // PV read address parts: lane i of group g addresses token 8 g + i / 2 of
