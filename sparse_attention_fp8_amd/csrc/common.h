@@ -104,11 +104,11 @@ __device__ __forceinline__ void seq_and_extent_wave(const BatchArgs& a, int r, i
 }
 
 // Order-preserving map float -> uint32 (larger float -> larger key), with -0
-// folded onto +0 so the two compare equal.
+// folded onto +0 (x + 0 is +0 for both zeros under round-to-nearest) so the
+// two compare equal.  NaN keeps its sign side: above +inf or below -inf.
 __device__ __forceinline__ uint32_t float_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u << 1) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return u ^ (uint32_t)(((int32_t)u >> 31) | (int32_t)0x80000000);
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

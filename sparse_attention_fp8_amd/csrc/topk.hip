@@ -70,8 +70,8 @@ struct TopkArgs {
 // with the copies innermost; its first kBins entries are reused by pass three
 // while hist2 serves pass two, so no pass clears a histogram it must wait for.
 struct Shared {
-  int hist1[kBins * kCopies];
-  int hist2[kBins];
+  int hist1[kBins * kCopies + 64];   // + one sink per lane for key 0 (never read)
+  int hist2[kBins + 64];             // + one sink per lane (never read)
   int out[DSA_MAX_TOPK];
   int wave_tot[kWaves];
   int misc[4];
@@ -161,15 +161,26 @@ __device__ void load_keys(Keys<KPT>& keys, const float* src, int n, float4* stag
     __builtin_amdgcn_s_waitcnt(0);
   }
   const int base = (int)threadIdx.x * KPT;
+  if (64 * KPT * (w + 1) <= n) {      // the whole wave lies inside the row: no range selects
 #pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int p = base + 4 * j;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (p < n) x = wst[l * V + (j ^ ((l / F) % V))];
-    keys.v[4 * j] = p < n ? float_key(x.x) : 0u;
-    keys.v[4 * j + 1] = p + 1 < n ? float_key(x.y) : 0u;
-    keys.v[4 * j + 2] = p + 2 < n ? float_key(x.z) : 0u;
-    keys.v[4 * j + 3] = p + 3 < n ? float_key(x.w) : 0u;
+    for (int j = 0; j < V; ++j) {
+      const float4 x = wst[l * V + (j ^ ((l / F) % V))];
+      keys.v[4 * j] = float_key(x.x);
+      keys.v[4 * j + 1] = float_key(x.y);
+      keys.v[4 * j + 2] = float_key(x.z);
+      keys.v[4 * j + 3] = float_key(x.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int p = base + 4 * j;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p < n) x = wst[l * V + (j ^ ((l / F) % V))];
+      keys.v[4 * j] = p < n ? float_key(x.x) : 0u;
+      keys.v[4 * j + 1] = p + 1 < n ? float_key(x.y) : 0u;
+      keys.v[4 * j + 2] = p + 2 < n ? float_key(x.z) : 0u;
+      keys.v[4 * j + 3] = p + 3 < n ? float_key(x.w) : 0u;
+    }
   }
   // materialise the keys here: otherwise the compiler sinks the range selects
   // into later loops and keeps one lane mask per key alive in scalar registers
@@ -233,11 +244,15 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist2[i] = 0;
   if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; }
   __syncthreads();
+  // Key 0 counts into a per-lane sink past the bins instead of branching
+  // around the atomic: a branch per key costs more than the select.
   const int copy = l & (kCopies - 1);
+  const int sink = kBins * kCopies + l;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint32_t key = keys.v[j];
-    if (key != 0u) atomicAdd(&sh.hist1[(int)(key >> 21) * kCopies + copy], 1);
+    const int addr = key != 0u ? (int)(key >> 21) * kCopies + copy : sink;
+    __hip_atomic_fetch_add(&sh.hist1[addr], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
   find_digit<kCopies>(sh.hist1, k, sh);
@@ -252,6 +267,8 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   constexpr int widths[2] = {11, 10};
   uint32_t mask = 0xFFE00000u;
   int* const hists[2] = {sh.hist2, sh.hist1};
+  // keys outside the prefix count into a per-lane sink (never read), as in pass one
+  int* const sinks[2] = {sh.hist2 + kBins + l, sh.hist1 + kBins * kCopies + l};
   __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
@@ -260,7 +277,8 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const uint32_t key = keys.v[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(int)((key >> shifts[pass]) & dmask)], 1);
+      int* const dst = (key & mask) == prefix ? hist + ((key >> shifts[pass]) & dmask) : sinks[pass];
+      __hip_atomic_fetch_add(dst, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     find_digit<1>(hist, rem, sh);
@@ -286,10 +304,16 @@ __device__ void stage_selected(const Keys<KPT>& keys, Selection sel, int k, Shar
   for (int i = threadIdx.x; i < k; i += kThreads) sh.out[i] = -1;
   MaskT<KPT> gtb = 0, eqb = 0;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t key = keys.v[j];
-    gtb |= (MaskT<KPT>)(key > sel.threshold) << j;
-    eqb |= (MaskT<KPT>)(key == sel.threshold) << j;
+  for (int j = 0; j < KPT; ++j) gtb |= (MaskT<KPT>)(keys.v[j] > sel.threshold) << j;
+  // Ties matter only when some are taken, and then only in waves holding one.
+  if (sel.need_eq > 0) {
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) any |= keys.v[j] == sel.threshold;
+    if (__ballot(any) != 0ull) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) eqb |= (MaskT<KPT>)(keys.v[j] == sel.threshold) << j;
+    }
   }
   const int ng = popc(gtb), ne = popc(eqb);
   const int packed = ng | (ne << 12);
