@@ -48,7 +48,8 @@ constexpr int kChunk = 32768;          // keys per workgroup in the row pass
 constexpr int kMergeMax = 65536;       // candidates per row in the merge pass
 constexpr int kGroupChunks = 4;        // chunks one group merge reduces to k candidates
 constexpr int kBins = 2048;
-constexpr int kCopies = 8;             // interleaved copies of the pass-one histogram
+constexpr int kCopies = 8;             // copies of the pass-one histogram
+constexpr int kCopyStride = kBins + 8;  // ints between copies: copy c of bin b sits in bank (8 c + b) % 64
 
 struct TopkArgs {
   BatchArgs batch;
@@ -66,11 +67,12 @@ struct TopkArgs {
   int32_t* grp_count;     // [R, ngroups]
 };
 
-// Selection state of one workgroup.  hist1 is pass one's histogram, bin-major
-// with the copies innermost; its first kBins entries are reused by pass three
-// while hist2 serves pass two, so no pass clears a histogram it must wait for.
+// Selection state of one workgroup.  hist1 is pass one's histogram, copy-major
+// with a padded stride (the copies of a bin, and bins 8 apart in one copy, sit
+// in different banks); its first kBins entries are reused by pass three while
+// hist2 serves pass two, so no pass clears a histogram it must wait for.
 struct Shared {
-  int hist1[kBins * kCopies + 64];   // + one sink per lane for key 0 (never read)
+  int hist1[kCopies * kCopyStride + 64];   // + one sink per lane for key 0 (never read)
   int hist2[kBins + 64];             // + one sink per lane (never read)
   int out[DSA_MAX_TOPK];
   int wave_tot[kWaves];
@@ -204,17 +206,19 @@ struct Selection {
 };
 
 // Finds the threshold digit of one pass from a histogram (bins in ascending
-// digit order, NC interleaved copies per bin): the digit d whose bin holds
+// digit order, NC copies kCopyStride ints apart): the digit d whose bin holds
 // the rem-th largest counted key, the count of keys above its bin, and its
-// bin count -> sh.misc[0..2].  Thread t takes bins 2047 - 2t and 2046 - 2t.
+// bin count -> sh.misc[0..2].  Thread t takes bins 2047 - 2t and 2046 - 2t,
+// one 8-byte read per copy (consecutive lanes read consecutive 8 bytes).
 template <int NC>
 __device__ __forceinline__ void find_digit(const int* hist, int rem, Shared& sh) {
   const int d0 = kBins - 1 - 2 * (int)threadIdx.x, d1 = d0 - 1;
   int c0 = 0, c1 = 0;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    c0 += hist[d0 * NC + c];
-    c1 += hist[d1 * NC + c];
+    const int2 v = *reinterpret_cast<const int2*>(hist + c * kCopyStride + d1);
+    c1 += v.x;
+    c0 += v.y;
   }
   const int incl = block_scan(c0 + c1, sh);
   const int excl = incl - c0 - c1;
@@ -239,7 +243,7 @@ __device__ __forceinline__ void find_digit(const int* hist, int rem, Shared& sh)
 template <int KPT>
 __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   const int l = lane_id();
-  for (int i = threadIdx.x; i < kBins * kCopies / 4; i += kThreads)
+  for (int i = threadIdx.x; i < kCopies * kCopyStride / 4; i += kThreads)
     reinterpret_cast<int4*>(sh.hist1)[i] = make_int4(0, 0, 0, 0);
   for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist2[i] = 0;
   if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; }
@@ -247,11 +251,11 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   // Key 0 counts into a per-lane sink past the bins instead of branching
   // around the atomic: a branch per key costs more than the select.
   const int copy = l & (kCopies - 1);
-  const int sink = kBins * kCopies + l;
+  const int sink = kCopies * kCopyStride + l;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint32_t key = keys.v[j];
-    const int addr = key != 0u ? (int)(key >> 21) * kCopies + copy : sink;
+    const int addr = key != 0u ? copy * kCopyStride + (int)(key >> 21) : sink;
     __hip_atomic_fetch_add(&sh.hist1[addr], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
@@ -268,7 +272,7 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   uint32_t mask = 0xFFE00000u;
   int* const hists[2] = {sh.hist2, sh.hist1};
   // keys outside the prefix count into a per-lane sink (never read), as in pass one
-  int* const sinks[2] = {sh.hist2 + kBins + l, sh.hist1 + kBins * kCopies + l};
+  int* const sinks[2] = {sh.hist2 + kBins + l, sh.hist1 + kCopies * kCopyStride + l};
   __syncthreads();
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
