@@ -142,8 +142,13 @@ __device__ __forceinline__ int block_scan(int v, Shared& sh) {
 // Float4s at or past n are not read (their slot gets a copy of the row's first
 // float4 and is masked afterwards); src is 16-byte aligned and every float4
 // that starts below n lies inside the row.
-template <int KPT>
-__device__ void load_keys(Keys<KPT>& keys, const float* src, int n, float4* stage) {
+// A staged value as a key: logits go through float_key, candidate keys (RAW)
+// are already keys.
+template <bool RAW>
+__device__ __forceinline__ uint32_t to_key(float x) { return RAW ? __float_as_uint(x) : float_key(x); }
+
+template <int KPT, bool RAW = false>
+__device__ void load_keys(Keys<KPT>& keys, const void* src, int n, float4* stage) {
   constexpr int V = KPT / 4;
   constexpr int F = 16 / V;
   const int w = threadIdx.x >> 6, l = lane_id();
@@ -167,10 +172,10 @@ __device__ void load_keys(Keys<KPT>& keys, const float* src, int n, float4* stag
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const float4 x = wst[l * V + (j ^ ((l / F) % V))];
-      keys.v[4 * j] = float_key(x.x);
-      keys.v[4 * j + 1] = float_key(x.y);
-      keys.v[4 * j + 2] = float_key(x.z);
-      keys.v[4 * j + 3] = float_key(x.w);
+      keys.v[4 * j] = to_key<RAW>(x.x);
+      keys.v[4 * j + 1] = to_key<RAW>(x.y);
+      keys.v[4 * j + 2] = to_key<RAW>(x.z);
+      keys.v[4 * j + 3] = to_key<RAW>(x.w);
     }
   } else {
 #pragma unroll
@@ -178,10 +183,10 @@ __device__ void load_keys(Keys<KPT>& keys, const float* src, int n, float4* stag
       const int p = base + 4 * j;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (p < n) x = wst[l * V + (j ^ ((l / F) % V))];
-      keys.v[4 * j] = p < n ? float_key(x.x) : 0u;
-      keys.v[4 * j + 1] = p + 1 < n ? float_key(x.y) : 0u;
-      keys.v[4 * j + 2] = p + 2 < n ? float_key(x.z) : 0u;
-      keys.v[4 * j + 3] = p + 3 < n ? float_key(x.w) : 0u;
+      keys.v[4 * j] = p < n ? to_key<RAW>(x.x) : 0u;
+      keys.v[4 * j + 1] = p + 1 < n ? to_key<RAW>(x.y) : 0u;
+      keys.v[4 * j + 2] = p + 2 < n ? to_key<RAW>(x.z) : 0u;
+      keys.v[4 * j + 3] = p + 3 < n ? to_key<RAW>(x.w) : 0u;
     }
   }
   // materialise the keys here: otherwise the compiler sinks the range selects
@@ -190,7 +195,8 @@ __device__ void load_keys(Keys<KPT>& keys, const float* src, int n, float4* stag
   for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(keys.v[j]));
 }
 
-// Candidate keys (4-byte aligned only: a row's candidates start at r * k).
+// Candidate keys read directly (per-thread strided loads), for candidate
+// counts whose staging would not fit in LDS.
 template <int KPT>
 __device__ void load_raw_keys(Keys<KPT>& keys, const uint32_t* src, int n) {
   const int base = (int)threadIdx.x * KPT;
@@ -404,7 +410,8 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
 // the row's top k is in the top k of its group.
 template <int KPT>
 __global__ void __launch_bounds__(kThreads) topk_group_kernel(TopkArgs a) {
-  __shared__ Shared sh;
+  __shared__ TopkLds<KPT> lds;
+  Shared& sh = lds.s;
   const int r = blockIdx.x / a.ngroups;
   const int g = blockIdx.x % a.ngroups;
   int b, e;
@@ -432,7 +439,8 @@ __global__ void __launch_bounds__(kThreads) topk_group_kernel(TopkArgs a) {
     return;
   }
   Keys<KPT> keys;
-  load_raw_keys(keys, ck, n);
+  load_keys<KPT, true>(keys, ck, n, lds.stage);   // candidate slots are 8 KB aligned
+  __syncthreads();   // every wave has read its keys: the staging area is free
   const Selection sel = radix_select(keys, k, sh);
   stage_selected(keys, sel, k, sh);
   for (int i = threadIdx.x; i < k; i += kThreads) {
@@ -447,7 +455,9 @@ __global__ void __launch_bounds__(kThreads) topk_group_kernel(TopkArgs a) {
 // group candidates when the merge has two levels.
 template <int KPT>
 __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
-  __shared__ Shared sh;
+  constexpr bool kStaged = KPT <= 32;   // 64 keys per thread would need 256 KB of staging
+  __shared__ TopkLds<kStaged ? KPT : 4> lds;
+  Shared& sh = lds.s;
   const int r = blockIdx.x;
   int b, e;
   seq_and_extent_wave(a.batch, r, b, e);
@@ -473,7 +483,12 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
   }
   int32_t* out = a.indices + (int64_t)r * k;
   Keys<KPT> keys;
-  load_raw_keys(keys, ck, n);
+  if constexpr (kStaged) {
+    load_keys<KPT, true>(keys, ck, n, lds.stage);   // candidate slots are 8 KB aligned
+    __syncthreads();   // every wave has read its keys: the staging area is free
+  } else {
+    load_raw_keys(keys, ck, n);
+  }
   const Selection sel = radix_select(keys, k, sh);
   stage_selected(keys, sel, k, sh);
   for (int i = threadIdx.x; i < k; i += kThreads) {
