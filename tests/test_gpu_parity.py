@@ -202,11 +202,13 @@ def test_topk_forced_ties(dsa, pool):
     check_topk(got, host, wl, 2048)
 
 
-@pytest.mark.parametrize("L", [2_000_000, 600_000, 140_000])
+@pytest.mark.parametrize("L", [4_194_304, 2_000_000, 600_000, 140_000])
 def test_topk_long_rows_merge(dsa, L):
     """Rows far past one 32768-key chunk: many chunks feed the candidate merge,
-    through a group level past four chunks (2M keys: 62 chunks, 16 groups);
-    values repeat heavily, so ties decide much of the selection."""
+    through a group level past four chunks (2M keys: 62 chunks, 16 groups;
+    the 4,194,304-key maximum: 128 chunks, 32 groups, 65536 candidates in the
+    final merge, which reads them without LDS staging); values repeat heavily,
+    so ties decide much of the selection."""
     import sparse_attention_fp8_amd as lib
     lens = [L, L - 1000, 5000]
     qs = [0, 1, 2, 3]
