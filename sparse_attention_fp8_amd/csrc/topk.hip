@@ -16,11 +16,16 @@
 //    conflicts (a direct per-thread float4 read would touch 64 cache lines
 //    per wave instruction).
 //  * Up to three digit passes (11, 11 and 10 bits).  Pass one counts every
-//    key into 8 interleaved copies of a 2048-bin LDS histogram (lane l adds
-//    to copy l % 8), which spreads the atomics of the few hot bins; a block
+//    key into 8 copies of a 2048-bin LDS histogram (lane l adds to copy
+//    l % 8), which spreads the atomics of the few hot bins; the copies are
+//    stored copy-major with a padded stride, so the digit search reads each
+//    thread's two bins of a copy as one conflict-free 8-byte load.  A block
 //    scan over the bins from the top finds the threshold bin.  A pass stops
 //    the search when the threshold bin is taken whole.  Passes two and three
 //    rescan the registers, counting only keys that match the prefix so far.
+//    Every pass is branch-free: keys that do not count go to a per-lane sink
+//    past the bins.  The candidate merges stage their keys through LDS the
+//    same way as the row pass.
 //  * Emission: each thread forms bit masks of its keys above the threshold
 //    and equal to it; one block scan gives every thread its output offset and
 //    tie budget; each thread walks the set bits of its mask, so it writes
