@@ -45,26 +45,44 @@ __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   return r;
 }
 
-// N-way merge of the split partials: one wave per (row, head), 8 dims per lane.
-// Every load goes out before any is used -- the split maxima and sums
-// (lane-parallel, lane i <-> split i) and the accumulators of the first U
-// splits -- so the merge costs one memory round trip, not two.
+// N-way merge of the split partials.  A (row, head) pair is spread over
+// 8 / DPL waves, each lane merging DPL consecutive dims, and a wave keeps
+// U = 64 / DPL splits in flight (64 accumulator values per lane): every load
+// of a round goes out before any is used -- the split maxima and sums
+// (lane-parallel, lane i <-> split i) and the accumulators of U splits -- so
+// up to U splits cost one memory round trip.  The launcher picks the smallest
+// DPL that still holds every split in one round (8 splits: one wave per pair
+// with 8 dims per lane; 32 splits: four waves per pair with 2 dims per lane).
+template <int DPL>
 __global__ void __launch_bounds__(256) sparse_mla_merge_kernel(MlaArgs a) {
+  static_assert(DPL == 2 || DPL == 4 || DPL == 8, "dims per lane");
+  constexpr int WPP = 8 / DPL;        // waves per (row, head) pair
+  constexpr int U = 64 / DPL;         // splits per load round
   const int R = a.batch.num_rows;
-  const int64_t pair = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t pair = gw / WPP;
   if (pair >= (int64_t)R * a.H) return;
   const int lane = lane_id();
+  const int d0 = (int)(gw % WPP) * (64 * DPL) + DPL * lane;
   const int64_t RH = (int64_t)R * a.H;
-  constexpr int U = 8;
-  float4 x[U][2];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (u < a.splits) {
-      const float4* src = reinterpret_cast<const float4*>(a.part_acc + (u * RH + pair) * kVDim + 8 * lane);
-      x[u][0] = src[0];
-      x[u][1] = src[1];
+  float x[U][DPL];
+  auto load = [&](int u, int split) __attribute__((always_inline)) {
+    const float* src = a.part_acc + (split * RH + pair) * kVDim + d0;
+    if constexpr (DPL == 8) {
+      const float4 v0 = reinterpret_cast<const float4*>(src)[0], v1 = reinterpret_cast<const float4*>(src)[1];
+      x[u][0] = v0.x; x[u][1] = v0.y; x[u][2] = v0.z; x[u][3] = v0.w;
+      x[u][4] = v1.x; x[u][5] = v1.y; x[u][6] = v1.z; x[u][7] = v1.w;
+    } else if constexpr (DPL == 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src);
+      x[u][0] = v.x; x[u][1] = v.y; x[u][2] = v.z; x[u][3] = v.w;
+    } else {
+      const float2 v = *reinterpret_cast<const float2*>(src);
+      x[u][0] = v.x; x[u][1] = v.y;
     }
-  }
+  };
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u < a.splits) load(u, u);
   float mi = kMaskSentinel, li = 0.f;
   if (lane < a.splits) {
     mi = a.part_ml[(lane * RH + pair) * 2];
@@ -73,36 +91,47 @@ __global__ void __launch_bounds__(256) sparse_mla_merge_kernel(MlaArgs a) {
   const float M = wave_max(mi);
   const float wi = li > 0.f ? exp2f(mi - M) : 0.f;
   const float L = wave_sum(li * wi);
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float o[DPL];
+#pragma unroll
+  for (int d = 0; d < DPL; ++d) o[d] = 0.f;
   for (int i0 = 0; i0 < a.splits; i0 += U) {
     if (i0 > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (i0 + u < a.splits) {
-          const float4* src =
-              reinterpret_cast<const float4*>(a.part_acc + ((i0 + u) * RH + pair) * kVDim + 8 * lane);
-          x[u][0] = src[0];
-          x[u][1] = src[1];
-        }
-      }
+      for (int u = 0; u < U; ++u)
+        if (i0 + u < a.splits) load(u, i0 + u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (i0 + u < a.splits) {
         const float wgt = __shfl(wi, i0 + u, 64);
-        o[0] += wgt * x[u][0].x; o[1] += wgt * x[u][0].y; o[2] += wgt * x[u][0].z; o[3] += wgt * x[u][0].w;
-        o[4] += wgt * x[u][1].x; o[5] += wgt * x[u][1].y; o[6] += wgt * x[u][1].z; o[7] += wgt * x[u][1].w;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) o[d] += wgt * x[u][d];
       }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint4 pk;
-  pk.x = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
-  pk.y = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
-  pk.z = (uint32_t)f32_to_bf16_rne(o[4] * inv) | ((uint32_t)f32_to_bf16_rne(o[5] * inv) << 16);
-  pk.w = (uint32_t)f32_to_bf16_rne(o[6] * inv) | ((uint32_t)f32_to_bf16_rne(o[7] * inv) << 16);
-  *reinterpret_cast<uint4*>(a.out + pair * kVDim + 8 * lane) = pk;
-  if (lane == 0) a.lse[pair] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  uint32_t pk[DPL / 2];
+#pragma unroll
+  for (int d = 0; d < DPL / 2; ++d)
+    pk[d] = (uint32_t)f32_to_bf16_rne(o[2 * d] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * d + 1] * inv) << 16);
+  uint16_t* dst = a.out + pair * kVDim + d0;
+  if constexpr (DPL == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  else if constexpr (DPL == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+  else *reinterpret_cast<uint32_t*>(dst) = pk[0];
+  if (lane == 0 && gw % WPP == 0) a.lse[pair] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Launch of the merge for R rows of H heads over `splits` partials.
+__host__ inline hipError_t launch_sparse_mla_merge(const MlaArgs& a, int splits, hipStream_t stream) {
+  const int64_t pairs = (int64_t)a.batch.num_rows * a.H;
+  if (splits <= 8) {
+    hipLaunchKernelGGL(sparse_mla_merge_kernel<8>, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, a);
+  } else if (splits <= 16) {
+    hipLaunchKernelGGL(sparse_mla_merge_kernel<4>, dim3((unsigned)((pairs + 1) / 2)), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(sparse_mla_merge_kernel<2>, dim3((unsigned)pairs), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace

@@ -468,9 +468,7 @@ hipError_t launch_sparse_mla_fp8(const BatchArgs& batch, const uint16_t* q, int 
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
-  const int64_t pairs = (int64_t)batch.num_rows * H;
-  hipLaunchKernelGGL(sparse_mla_merge_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_sparse_mla_merge(a, p.splits, stream);
 }
 
 }  // namespace dsa

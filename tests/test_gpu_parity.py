@@ -260,7 +260,7 @@ def run_mla(dsa, wl, batch, t, idx, splits):
     return out, lse
 
 
-@pytest.mark.parametrize("splits", [0, 1, 2, 3, 16, 32])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 12, 16, 32])
 @pytest.mark.parametrize("H", [16, 32, 64, 128])
 def test_sparse_mla_parity(dsa, H, splits):
     wl, batch, t, idx = mla_inputs(dsa, [3000, 700, 130, 2049], [1, 2, 1, 1], H, seed=H + splits)
