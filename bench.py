@@ -126,19 +126,32 @@ def cpu_baseline(wl, budget_s):
     bt, sl, qs = wl.block_table.numpy(), wl.seq_lens.numpy(), wl.query_start.numpy()
     qm, kv = wl.q_mla.view(torch.int16).numpy(), wl.kv_cache.view(torch.int16).numpy()
     stride = wl.max_seq_len
-    done, t0 = 0, time.perf_counter()
-    for r in order:
-        lg, _, _ = oracle.indexer_logits(q8, w, cache, bt, sl, qs, stride, rows=[int(r)])
-        idx = oracle.topk(lg, sl, qs, wl.topk, rows=[int(r)])
-        oracle.sparse_mla(qm, kv, bt, sl, qs, idx, wl.softmax_scale, rows=[int(r)])
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    # Rows in a seeded order until the budget runs out; a step that finishes
+    # early is repeated until at least half the budget is spent, so the
+    # figure averages over several seconds of work.
+    done, passes, t0 = 0, 0, time.perf_counter()
+    out_of_time = False
+    while not out_of_time:
+        for r in order:
+            lg, _, _ = oracle.indexer_logits(q8, w, cache, bt, sl, qs, stride, rows=[int(r)])
+            idx = oracle.topk(lg, sl, qs, wl.topk, rows=[int(r)])
+            oracle.sparse_mla(qm, kv, bt, sl, qs, idx, wl.softmax_scale, rows=[int(r)])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                out_of_time = True
+                break
+        else:
+            passes += 1
+            out_of_time = time.perf_counter() - t0 > budget_s / 2
     dt = time.perf_counter() - t0
     steps_per_s = (done / R) / dt
-    return {"value": steps_per_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {R} rows of one step (indexer+top-k+sparse MLA per row, float64 numpy), "
-                      f"{dt:.1f} s, scaled by {R}/{done}"}
+    if passes >= 1:
+        sample = (f"{passes} whole step(s) plus {done - passes * R} rows, {done} rows in all "
+                  f"(indexer+top-k+sparse MLA per row, float64 numpy), {dt:.1f} s")
+    else:
+        sample = (f"{done} of {R} rows of one step (indexer+top-k+sparse MLA per row, float64 numpy), "
+                  f"{dt:.1f} s, scaled by {R}/{done}")
+    return {"value": steps_per_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle", "sample": sample}
 
 
 def pre_path(dsa, wl, batch_dev, base, dev, steps):
