@@ -13,10 +13,11 @@
 //      16 heads:  4 waves, each scores 16 of the tile's 64 tokens and
 //                 accumulates 128 of the 512 output dims;
 //      32 heads:  4 waves = 2 head tiles x 2 parts (32 tokens / 256 dims each);
-//      >=64 heads: 8 waves = 4 head tiles x 2 parts, 64-head blocks.
-//    Scores of a head tile are computed once; the tile maximum and the bf16
-//    probabilities are exchanged through LDS between the waves of that head
-//    tile, and every wave accumulates its own dims over all 64 tokens.
+//      >=64 heads: 8 waves = 4 head tiles x 2 parts, 64-head blocks; in PV
+//      each wave instead takes two head tiles over 128 dims.
+//    Scores of a head tile are computed once; the tile maxima and the bf16
+//    probabilities are exchanged through LDS between the waves, and every
+//    wave accumulates its own (heads, dims) block over all 64 tokens.
 //  * Gather: the 64 selected latent rows of a tile (64 x 1152 B) are copied
 //    from HBM straight into LDS with global_load_lds_dwordx4 into two buffers.
 //    With 16 heads the copy of tile i+2 is issued as soon as tile i's buffer
@@ -79,17 +80,27 @@ struct MlaShared {
 // than the second tile in flight saves (measured: 64 heads over 128 rows,
 // 87.6 us one ahead against 96.8 us two ahead; 32 heads over 32 rows, 31.8
 // against 33.6 us; 16 heads over the same rows, 27.0 against 25.8 us).
-template <int HT, int TP, bool DEEP>
+//
+// PVH: head tiles per wave in PV.  QK keeps one 16-head tile per wave (its q
+// operand takes 72 VGPRs), but a PV wave can take PVH head tiles over fewer
+// dims, so that each transposed V^T read feeds PVH MFMAs.  With four head
+// tiles the QK and PV phases both run at the LDS bandwidth (operand reads
+// plus the next tile's copy), and PVH = 2 halves PV's share.
+template <int HT, int TP, bool DEEP, int PVH>
 __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   constexpr int NW = HT * TP;          // waves
   constexpr int TPT = 4 / TP;          // token tiles of 16 scored per wave
-  constexpr int DW = kVDim / TP;       // output dims per wave
+  constexpr int HGP = HT / PVH;        // head groups in PV
+  constexpr int TPV = NW / HGP;        // dim parts in PV
+  constexpr int DW = kVDim / TPV;      // output dims per wave
   constexpr int NDT = DW / 16;         // dim tiles per wave
   constexpr int RGW = kRowGroups / NW; // row groups each wave gathers
   constexpr int ND = RGW * kChunkGroups;   // gather loads per wave and tile
   static_assert(RGW * NW == kRowGroups, "waves must split the row groups evenly");
   static_assert(DW % 128 == 0, "PV swizzle terms assume 128-dim aligned parts");
   static_assert(ND + 2 < 64, "vmcnt range");
+  static_assert(HGP * PVH == HT && TPV * HGP == NW, "PV roles must cover heads and dims");
+  static_assert(TP > 1, "the tile maxima and sums are exchanged through LDS");
   __shared__ MlaShared<HT, TP> sh;
 
   const int R = a.batch.num_rows;
@@ -108,7 +119,9 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 
   const int ht = wave % HT, part = wave / HT;
   const int h = hb * (16 * HT) + ht * 16 + n16;
-  const int d_base = part * DW;
+  const int hgp = wave % HGP, dpart = wave / HGP;
+  const int hp0 = hb * (16 * HT) + hgp * (16 * PVH) + n16;
+  const int d_base = dpart * DW;
 
   const int slot0 = sp * a.split_slots;
   const int slot1 = min(slot0 + a.split_slots, a.k);
@@ -197,7 +210,6 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   // chunk 4 ks + g; the swizzle term is x0 for even ks and x0 ^ 64 for odd.
   const int r8 = n16 & 7;
   const int qk0 = (n16 >> 3) * 1024 + r8 * 128 + (((g ^ r8) << 4));
-  const int qk1 = (n16 >> 3) * 1024 + r8 * 128 + (((g ^ r8) << 4) ^ 64);
   // PV: the V^T operand comes from two transposed reads per MFMA.  Lane n16
   // of group g addresses token 32 tp + 4 g + n16 / 4 (+16 for the second
   // read), dims d_base + 16 dt + 4 (n16 % 4) .. +3, so after the transpose it
@@ -207,9 +219,14 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   const int pv_lane = (g >> 1) * 1024 + (((g & 1) << 2) + (n16 >> 2)) * 128 + 8 * (n16 & 1);
   const int pv_part = (d_base >> 6) * (kRowGroups * 1024);
 
-  v4f acc[NDT];
+  v4f acc[PVH][NDT];
+  float m_pv[PVH];
 #pragma unroll
-  for (int i = 0; i < NDT; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < PVH; ++hh) {
+#pragma unroll
+    for (int i = 0; i < NDT; ++i) acc[hh][i] = v4f{0.f, 0.f, 0.f, 0.f};
+    m_pv[hh] = kMaskSentinel;
+  }
   float m_run = kMaskSentinel;   // running max of the log2-domain scores of head h
   float l_part = 0.f;            // this lane's share of the running sum
 
@@ -271,7 +288,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
           for (int i = 0; i < ND; ++i)
             if (i * NQ / ND == q && pre) gather_one(i);
-          const unsigned char* cb = tile + ((ks & 1) ? qk1 : qk0) + (ks >> 1) * (kRowGroups * 1024) + tt * 2048;
+          const unsigned char* cb = tile + (qk0 ^ ((ks & 1) << 6)) + (ks >> 1) * (kRowGroups * 1024) + tt * 2048;
           const uint4 cv = *reinterpret_cast<const uint4*>(cb);
           s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(cv), as_v8bf(qreg[ks]), s[u], 0, 0, 0);
         }
@@ -287,17 +304,39 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
           s[u][i] = z;
           tmax = fmaxf(tmax, z);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      if (TP > 1) {
-        if (g == 0) sh.tmax[ht][part][n16] = tmax;
-        __syncthreads();
-#pragma unroll
-        for (int pp = 0; pp < TP; ++pp) tmax = fmaxf(tmax, sh.tmax[ht][pp][n16]);
+      tmax = fmaxf(tmax, lane_xor16(tmax));
+      tmax = fmaxf(tmax, lane_xor32(tmax));
+      if (g == 0) {
+        // The address is formed here rather than held across the loop: at
+        // 256 VGPRs the compiler otherwise spills it, and the reload's
+        // vmcnt(0) would wait for the next tile's copy.
+        int n = n16;
+        asm volatile("" : "+v"(n));
+        sh.tmax[ht][part][n] = tmax;
       }
+      __syncthreads();
+#pragma unroll
+      for (int pp = 0; pp < TP; ++pp) tmax = fmaxf(tmax, sh.tmax[ht][pp][n16]);
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
+      // v_exp_f32 directly: exp2f's extra scaling only matters for results
+      // below 2^-126, which are nothing next to the running maximum's 1.
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      float alpha_pv[PVH];
+      if constexpr (PVH == 1) {
+        alpha_pv[0] = alpha;
+        m_pv[0] = m_new;
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < PVH; ++hh) {
+          float tm = kMaskSentinel;
+#pragma unroll
+          for (int pp = 0; pp < TP; ++pp) tm = fmaxf(tm, sh.tmax[hgp * PVH + hh][pp][n16]);
+          const float mn = fmaxf(m_pv[hh], tm);
+          alpha_pv[hh] = __builtin_amdgcn_exp2f(m_pv[hh] - mn);
+          m_pv[hh] = mn;
+        }
+      }
       float psum = 0.f;
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
@@ -307,7 +346,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int tok = (part * TPT + u) * 16 + 4 * g + i;
           const bool v = (mask >> tok) & 1ull;
-          pv[i] = v ? exp2f(s[u][i] - m_new) : 0.f;
+          pv[i] = v ? __builtin_amdgcn_exp2f(s[u][i] - m_new) : 0.f;
           psum += pv[i];
         }
         v4bf16 b4;
@@ -317,7 +356,9 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
       }
       l_part = l_part * alpha + psum;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      for (int hh = 0; hh < PVH; ++hh)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[hh][dt] *= alpha_pv[hh];
       __syncthreads();                                 // probabilities of all token tiles
 
       // O^T += V^T . P^T over the 64 tokens, 32 per MFMA: k slot i of lane group
@@ -325,10 +366,14 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
       const unsigned char* pv_base = tile + pv_part + pv_lane;
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        const uint2 pa = sh.p[ht][2 * tp][g][n16];
-        const uint2 pb2 = sh.p[ht][2 * tp + 1][g][n16];
-        uint4 pcat = make_uint4(pa.x, pa.y, pb2.x, pb2.y);
-        const v8bf pb = as_v8bf(pcat);
+        v8bf pb[PVH];
+#pragma unroll
+        for (int hh = 0; hh < PVH; ++hh) {
+          const uint2 pa = sh.p[hgp * PVH + hh][2 * tp][g][n16];
+          const uint2 pb2 = sh.p[hgp * PVH + hh][2 * tp + 1][g][n16];
+          uint4 pcat = make_uint4(pa.x, pa.y, pb2.x, pb2.y);
+          pb[hh] = as_v8bf(pcat);
+        }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const unsigned char* vb = pv_base + (dt >> 2) * (kRowGroups * 1024) + tp * 4096 +
@@ -338,7 +383,9 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
           const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           v8bf va;
           __builtin_memcpy(&va, &vv, 16);
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[dt], 0, 0, 0);
+#pragma unroll
+          for (int hh = 0; hh < PVH; ++hh)
+            acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh], acc[hh][dt], 0, 0, 0);
         }
       }
     }
@@ -354,39 +401,45 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
     }
   }
 
-  // l of head h over all tokens: lane groups, then the parts of the head tile
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (TP > 1) {
+  // l of each PV head over all tokens: lane groups, then the parts of its head tile
+  {
+    const float l_own = l_part + lane_xor16(l_part);
+    const float l_sum = l_own + lane_xor32(l_own);
     __syncthreads();
-    if (g == 0) sh.tmax[ht][part][n16] = l_tot;
+    if (g == 0) sh.tmax[ht][part][n16] = l_sum;
     __syncthreads();
-    l_tot = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < TP; ++pp) l_tot += sh.tmax[ht][pp][n16];
   }
-
-  if (a.splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = a.out + ((int64_t)r * a.H + h) * kVDim + d_base + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16_rne(acc[dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[dt][1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16_rne(acc[dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(op + dt * 16) = pk;
-    }
-    if (part == 0 && g == 0)
-      a.lse[(int64_t)r * a.H + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    const int64_t base = ((int64_t)sp * R + r) * a.H + h;
-    float* pa = a.part_acc + base * kVDim + d_base + 4 * g;
+  for (int hh = 0; hh < PVH; ++hh) {
+    float l_tot = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-      *reinterpret_cast<float4*>(pa + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (part == 0 && g == 0) {
-      a.part_ml[base * 2] = l_tot > 0.f ? m_run : kMaskSentinel;
-      a.part_ml[base * 2 + 1] = l_tot;
+    for (int pp = 0; pp < TP; ++pp) l_tot += sh.tmax[hgp * PVH + hh][pp][n16];
+    const int hp = hp0 + 16 * hh;
+    if (a.splits == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      uint16_t* op = a.out + ((int64_t)r * a.H + hp) * kVDim + d_base + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const v4f o = acc[hh][dt];
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + dt * 16) = pk;
+      }
+      if (dpart == 0 && g == 0)
+        a.lse[(int64_t)r * a.H + hp] = l_tot > 0.f ? (m_pv[hh] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t base = ((int64_t)sp * R + r) * a.H + hp;
+      float* pa = a.part_acc + base * kVDim + d_base + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const v4f o = acc[hh][dt];
+        *reinterpret_cast<float4*>(pa + dt * 16) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (dpart == 0 && g == 0) {
+        a.part_ml[base * 2] = l_tot > 0.f ? m_pv[hh] : kMaskSentinel;
+        a.part_ml[base * 2 + 1] = l_tot;
+      }
     }
   }
 }
@@ -451,11 +504,11 @@ hipError_t launch_sparse_mla(const BatchArgs& batch, const uint16_t* q, int H, c
   const int64_t units = (int64_t)batch.num_rows * p.splits;
   const int64_t grid = (units + 7) / 8 * 8 * p.head_blocks;
   if (H == 16) {
-    hipLaunchKernelGGL((sparse_mla_kernel<1, 4, true>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<1, 4, true, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else if (H == 32) {
-    hipLaunchKernelGGL((sparse_mla_kernel<2, 2, false>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<2, 2, false, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((sparse_mla_kernel<4, 2, false>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<4, 2, false, 2>), dim3((unsigned)grid), dim3(512), 0, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;

@@ -332,16 +332,25 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
           z[u][i] = zz;
           tmax = fmaxf(tmax, zz);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = fmaxf(tmax, lane_xor16(tmax));
+      tmax = fmaxf(tmax, lane_xor32(tmax));
       if (TP > 1) {
-        if (g == 0) sh.tmax[ht][part][n16] = tmax;
+        if (g == 0) {
+          // The address is formed here rather than held across the loop: near
+          // the VGPR limit the compiler otherwise spills it, and the reload's
+          // vmcnt(0) would wait for the copies in flight.
+          int n = n16;
+          asm volatile("" : "+v"(n));
+          sh.tmax[ht][part][n] = tmax;
+        }
         __syncthreads();
 #pragma unroll
         for (int pp = 0; pp < TP; ++pp) tmax = fmaxf(tmax, sh.tmax[ht][pp][n16]);
       }
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
+      // v_exp_f32 directly: exp2f's extra scaling only matters for results
+      // below 2^-126, which are nothing next to the running maximum's 1.
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       float psum = 0.f;
 #pragma unroll
@@ -351,7 +360,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool v = (mask >> (tk0 + i)) & 1ull;
-          pv[i] = v ? exp2f(z[u][i] - m_new) : 0.f;
+          pv[i] = v ? __builtin_amdgcn_exp2f(z[u][i] - m_new) : 0.f;
           psum += pv[i];
         }
         // P'_c = p * scale_c for the 4 scale groups
@@ -394,8 +403,8 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
     }
   }
 
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  float l_tot = l_part + lane_xor16(l_part);
+  l_tot += lane_xor32(l_tot);
   if (TP > 1) {
     __syncthreads();
     if (g == 0) sh.tmax[ht][part][n16] = l_tot;
@@ -405,9 +414,15 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
     for (int pp = 0; pp < TP; ++pp) l_tot += sh.tmax[ht][pp][n16];
   }
 
+  // Output addresses from a lane index the compiler cannot see through, so
+  // they are formed here and not held (or spilled) across the tile loop.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int ho = hb * (16 * HT) + ht * 16 + (ln & 15);   // = h
+  const int go = ln >> 4;                                  // = g
   if (a.splits == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = a.out + ((int64_t)r * a.H + h) * kVDim + d_base + 4 * g;
+    uint16_t* op = a.out + ((int64_t)r * a.H + ho) * kVDim + d_base + 4 * go;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 pk;
@@ -415,15 +430,15 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
       pk.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
       *reinterpret_cast<uint2*>(op + dt * 16) = pk;
     }
-    if (part == 0 && g == 0)
-      a.lse[(int64_t)r * a.H + h] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (part == 0 && go == 0)
+      a.lse[(int64_t)r * a.H + ho] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
-    const int64_t base = ((int64_t)sp * R + r) * a.H + h;
-    float* pa = a.part_acc + base * kVDim + d_base + 4 * g;
+    const int64_t base = ((int64_t)sp * R + r) * a.H + ho;
+    float* pa = a.part_acc + base * kVDim + d_base + 4 * go;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
       *reinterpret_cast<float4*>(pa + dt * 16) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (part == 0 && g == 0) {
+    if (part == 0 && go == 0) {
       a.part_ml[base * 2] = l_tot > 0.f ? m_run : kMaskSentinel;
       a.part_ml[base * 2 + 1] = l_tot;
     }
