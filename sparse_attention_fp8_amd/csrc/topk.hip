@@ -22,7 +22,10 @@
 //    thread's two bins of a copy as one conflict-free 8-byte load.  A block
 //    scan over the bins from the top finds the threshold bin.  A pass stops
 //    the search when the threshold bin is taken whole.  Passes two and three
-//    rescan the registers, counting only keys that match the prefix so far.
+//    rescan the registers, counting only keys that match the prefix so far;
+//    when the bin left after pass two holds at most 64 keys (the usual case
+//    for real-valued logits), those keys are collected instead and ranked by
+//    one wave, which replaces pass three's rescan.
 //    Every pass is branch-free: keys that do not count go to a per-lane sink
 //    past the bins.  The candidate merges stage their keys through LDS the
 //    same way as the row pass.
@@ -82,6 +85,7 @@ struct Shared {
   int out[DSA_MAX_TOPK];
   int wave_tot[kWaves];
   int misc[4];
+  uint32_t cand[64];                 // keys of a small threshold bin after two digits
 };
 
 // The key staging area overlaps the selection state: it is dead once every
@@ -249,15 +253,59 @@ __device__ __forceinline__ void find_digit(const int* hist, int rem, Shared& sh)
 //  pass 1: 11-bit top digit of every key;
 //  passes 2 and 3 (11 and 10 bits) scan the registers again and count only
 //  the keys whose higher digits match the prefix found so far.  (Compacting
-//  the threshold bin into an LDS list first costs more than it saves: its
-//  per-key mask build and predicated stores take as long as both scans.)
+//  the threshold bin into an LDS list after pass 1 costs more than it saves:
+//  that bin holds thousands of keys.  After pass 2 it usually holds a few,
+//  and resolve_small_bin replaces pass 3.)
+//
+// The threshold bin after two digits holds at most 64 keys: they are
+// collected into LDS -- a ballot per key slot, so a wave without a matching
+// key in that slot skips it -- and one wave ranks them: the rem-th largest is
+// the threshold key, the bin's keys above it are taken whole and rem minus
+// their count of the keys equal to it.
+template <int KPT>
+__device__ Selection resolve_small_bin(const Keys<KPT>& keys, uint32_t prefix, uint32_t mask, int rem, Shared& sh) {
+  const int l = lane_id();
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool m = (keys.v[j] & mask) == prefix;
+    const uint64_t bal = __ballot(m);
+    if (bal != 0ull) {   // wave-uniform
+      int base = 0;
+      if (l == 0) base = __hip_atomic_fetch_add(&sh.misc[3], popc((uint64_t)bal), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      base = __builtin_amdgcn_readfirstlane(base);
+      const int pos = base + popc((uint64_t)(bal & ((1ull << l) - 1ull)));
+      if (m && pos < 64) sh.cand[pos] = keys.v[j];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int nb = min(sh.misc[3], 64);
+    const uint32_t x = l < nb ? sh.cand[l] : 0u;
+    int gt = 0, eq = 0;
+    for (int j = 0; j < nb; ++j) {
+      const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, j);
+      gt += y > x ? 1 : 0;
+      eq += y == x ? 1 : 0;
+    }
+    if (l < nb && gt < rem && rem <= gt + eq) {
+      // every key equal to x taken: the same selection as "above x - 1",
+      // which spares the staging its tie masks (x >= 2^21, no wrap)
+      const bool all = rem == gt + eq;
+      sh.misc[0] = (int)(all ? x - 1u : x);
+      sh.misc[1] = all ? 0 : rem - gt;
+    }
+  }
+  __syncthreads();
+  return Selection{(uint32_t)sh.misc[0], sh.misc[1]};
+}
+
 template <int KPT>
 __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   const int l = lane_id();
   for (int i = threadIdx.x; i < kCopies * kCopyStride / 4; i += kThreads)
     reinterpret_cast<int4*>(sh.hist1)[i] = make_int4(0, 0, 0, 0);
   for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist2[i] = 0;
-  if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; }
+  if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; sh.misc[3] = 0; }
   __syncthreads();
   // Key 0 counts into a per-lane sink past the bins instead of branching
   // around the atomic: a branch per key costs more than the select.
@@ -301,6 +349,7 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
     prefix |= (uint32_t)sh.misc[0] << shifts[pass];
     mask |= dmask << shifts[pass];
     if (rem == sh.misc[2]) return Selection{prefix - 1u, 0};
+    if (pass == 0 && sh.misc[2] <= 64) return resolve_small_bin(keys, prefix, mask, rem, sh);
   }
   return Selection{prefix, rem};
 }

@@ -222,6 +222,27 @@ def test_topk_long_rows_merge(dsa, L):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("dist", ["grid", "narrow"])
+@pytest.mark.parametrize("k", [2048, 700])
+def test_topk_small_bin_ties(dsa, dist, k):
+    """After two 11-bit digits the threshold bin usually holds a few keys (at
+    most 64), which are ranked in one wave instead of a third digit pass.
+    Every third key copies its left neighbour, so the tie rule decides inside
+    that bin: with logits on a 2^-10 grid each bin holds copies of one value;
+    with a narrow continuous distribution (1.5 + 0.05 N(0,1)) a bin holds a
+    few distinct values and their copies."""
+    lens = [2049, 3000, 9000, 16384, 24000, 32768]
+    wl = synth.make_workload(lens, [1] * len(lens), 16, seed=31, spare_pages=2)
+    batch, _ = to_dev(wl)
+    rng = np.random.default_rng(k + (1 if dist == "grid" else 2))
+    x = rng.normal(size=(len(lens), 32768))
+    host = (np.round(x * 1024.0) / 1024.0 if dist == "grid" else 1.5 + 0.05 * x).astype(np.float32)
+    host[:, 1::3] = host[:, 0:-1:3]
+    logits = torch.from_numpy(host).to(DEV)
+    got = run_topk(dsa, batch, logits, k)
+    check_topk(got, host, wl, k)
+
+
 def test_topk_ties_from_duplicated_pages(dsa):
     """Every logical block of a sequence maps to the same physical page, so the
     logits repeat every 64 keys: ties broken only by index."""
