@@ -80,21 +80,39 @@ struct TopkArgs {
 // in different banks); its first kBins entries are reused by pass three while
 // hist2 serves pass two, so no pass clears a histogram it must wait for.
 struct Shared {
+  // zeroed before a selection (kInitBytes): both histograms and misc
   int hist1[kCopies * kCopyStride + 64];   // + one sink per lane for key 0 (never read)
   int hist2[kBins + 64];             // + one sink per lane (never read)
+  int misc[4];
+  // the rest is written before it is read
   int out[DSA_MAX_TOPK];
   int wave_tot[kWaves];
-  int misc[4];
   uint32_t cand[64];                 // keys of a small threshold bin after two digits
 };
+constexpr int kInitBytes = (int)offsetof(Shared, out);
+static_assert(kInitBytes % 16 == 0, "zeroed with 16-byte stores");
 
 // The key staging area overlaps the selection state: it is dead once every
-// wave has read its keys back (a barrier separates the two uses).
+// wave has read its keys back (a barrier separates the two uses).  Wave w
+// stages its keys in bytes [w R, (w + 1) R) of it (R = 256 KPT), and nobody
+// else touches them, so each wave zeroes the selection state inside its own
+// region as soon as it has read its keys back, and the state past all the
+// regions is zeroed while the keys are in flight: the barrier that frees the
+// staging area also publishes the zeroed state.
 template <int KPT>
 union TopkLds {
   Shared s;
   float4 stage[kThreads * KPT / 4];
 };
+
+// Zeroes the part of the selection state in bytes [lo, hi) of the LDS union,
+// with threads tid, tid + nthr, ... of the caller's group.
+__device__ __forceinline__ void zero_state(void* lds, int lo, int hi, int tid, int nthr) {
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > kInitBytes ? kInitBytes : hi;
+  int4* p = reinterpret_cast<int4*>(lds);
+  for (int i = lo / 16 + tid; i < hi / 16; i += nthr) p[i] = make_int4(0, 0, 0, 0);
+}
 
 template <int KPT>
 struct Keys {
@@ -160,10 +178,13 @@ template <int KPT, bool RAW = false>
 __device__ void load_keys(Keys<KPT>& keys, const void* src, int n, float4* stage) {
   constexpr int V = KPT / 4;
   constexpr int F = 16 / V;
+  constexpr int kRegion = 64 * V * 16;             // staging bytes per wave
   const int w = threadIdx.x >> 6, l = lane_id();
   const float4* src4 = reinterpret_cast<const float4*>(src);
   float4* wst = stage + w * 64 * V;
   const int f0 = w * 64 * V;                       // first float4 of this wave
+  // selection state past every wave's staging region: no one stages there
+  if (kWaves * kRegion < kInitBytes) zero_state(stage, kWaves * kRegion, kInitBytes, threadIdx.x, kThreads);
   if (4 * f0 < n) {
     const uint32_t wdst = lds_addr(wst);
 #pragma unroll
@@ -202,12 +223,19 @@ __device__ void load_keys(Keys<KPT>& keys, const void* src, int n, float4* stage
   // into later loops and keeps one lane mask per key alive in scalar registers
 #pragma unroll
   for (int j = 0; j < KPT; ++j) asm volatile("" : "+v"(keys.v[j]));
+  // this wave's reads of its region are issued (and the LDS operations of a
+  // wave execute in order): zero the selection state that lies in it.  The
+  // memory clobber keeps the compiler from moving these int4 stores above the
+  // float4 reads of the same bytes.
+  asm volatile("" ::: "memory");
+  zero_state(stage, w * kRegion, (w + 1) * kRegion, l, 64);
 }
 
 // Candidate keys read directly (per-thread strided loads), for candidate
 // counts whose staging would not fit in LDS.
 template <int KPT>
-__device__ void load_raw_keys(Keys<KPT>& keys, const uint32_t* src, int n) {
+__device__ void load_raw_keys(Keys<KPT>& keys, const uint32_t* src, int n, void* lds) {
+  zero_state(lds, 0, kInitBytes, threadIdx.x, kThreads);
   const int base = (int)threadIdx.x * KPT;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) keys.v[j] = base + j < n ? src[base + j] : 0u;
@@ -299,14 +327,11 @@ __device__ Selection resolve_small_bin(const Keys<KPT>& keys, uint32_t prefix, u
   return Selection{(uint32_t)sh.misc[0], sh.misc[1]};
 }
 
+// Precondition: the selection state (first kInitBytes of sh) is zero and
+// visible to every thread (load_keys / load_raw_keys, then a barrier).
 template <int KPT>
 __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   const int l = lane_id();
-  for (int i = threadIdx.x; i < kCopies * kCopyStride / 4; i += kThreads)
-    reinterpret_cast<int4*>(sh.hist1)[i] = make_int4(0, 0, 0, 0);
-  for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist2[i] = 0;
-  if (threadIdx.x == 0) { sh.misc[0] = 0; sh.misc[1] = 0; sh.misc[2] = 0; sh.misc[3] = 0; }
-  __syncthreads();
   // Key 0 counts into a per-lane sink past the bins instead of branching
   // around the atomic: a branch per key costs more than the select.
   const int copy = l & (kCopies - 1);
@@ -541,7 +566,8 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
     load_keys<KPT, true>(keys, ck, n, lds.stage);   // candidate slots are 8 KB aligned
     __syncthreads();   // every wave has read its keys: the staging area is free
   } else {
-    load_raw_keys(keys, ck, n);
+    load_raw_keys(keys, ck, n, &sh);
+    __syncthreads();   // the zeroed selection state is visible
   }
   const Selection sel = radix_select(keys, k, sh);
   stage_selected(keys, sel, k, sh);
