@@ -347,6 +347,9 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   uint32_t prefix = (uint32_t)sh.misc[0] << 21;
   int rem = k - sh.misc[1];
   const int in_bin = sh.misc[2];
+  // No crossing: fewer than k keys are orderable (key 0 -- an out-of-range
+  // slot, or the all-ones NaN -- counts nowhere).  Take all of them.
+  if (in_bin == 0) return Selection{0u, 0};
   if (rem == in_bin) return Selection{prefix - 1u, 0};  // the whole bin is taken
 
   // pass three counts into hist1's first kBins entries
@@ -379,18 +382,18 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   return Selection{prefix, rem};
 }
 
-// Stages the selected keys' chunk positions in sh.out[0, k), in chunk order.
-// Per thread: masks of keys above the threshold (gt) and equal to it (eq);
-// one block scan of the packed counts (gt in the low 12 bits -- a prefix of gt
-// counts never exceeds k <= 2048 -- and eq above) gives the thread's output
-// offset and how many ties precede it.  The thread keeps its first
-// (need_eq - ties before it) eq keys and writes the set bits of the combined
-// mask in order.  Out-of-range slots (key 0) are never taken and positions are
-// clamped to k, so whatever the logits hold (NaN included) every staged
-// position is -1 or a valid key position.
-template <int KPT>
-__device__ void stage_selected(const Keys<KPT>& keys, Selection sel, int k, Shared& sh) {
-  for (int i = threadIdx.x; i < k; i += kThreads) sh.out[i] = -1;
+// Emits the selected keys' chunk positions in chunk order: emit(pos, i) for
+// output slot pos of chunk position i.  Per thread: masks of keys above the
+// threshold (gt) and equal to it (eq); one block scan of the packed counts (gt
+// in the low 12 bits -- a prefix of gt counts never exceeds k <= 2048 -- and
+// eq above) gives the thread's output offset and how many ties precede it.
+// The thread keeps its first (need_eq - ties before it) eq keys and emits the
+// set bits of the combined mask in order.  Out-of-range slots (key 0) are
+// never taken and slots are clamped to k.  Returns how many slots were
+// emitted: slots [0, that) each exactly once -- k, unless the row holds fewer
+// than k orderable keys (a float whose key is 0, such as the all-ones NaN).
+template <int KPT, class Emit>
+__device__ int emit_selected(const Keys<KPT>& keys, Selection sel, int k, Shared& sh, Emit emit) {
   MaskT<KPT> gtb = 0, eqb = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) gtb |= (MaskT<KPT>)(keys.v[j] > sel.threshold) << j;
@@ -406,7 +409,10 @@ __device__ void stage_selected(const Keys<KPT>& keys, Selection sel, int k, Shar
   }
   const int ng = popc(gtb), ne = popc(eqb);
   const int packed = ng | (ne << 12);
-  const int excl = block_scan(packed, sh) - packed;   // barrier inside: the -1 fill is done
+  const int excl = block_scan(packed, sh) - packed;   // barrier inside
+  int tot = 0;                                        // block totals (all wave sums are in)
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) tot += sh.wave_tot[i];
   const int g = excl & 0xFFF;
   const int e = excl >> 12;
   int take = sel.need_eq - e;                         // ties this thread may take
@@ -418,10 +424,19 @@ __device__ void stage_selected(const Keys<KPT>& keys, Selection sel, int k, Shar
   const int base = (int)threadIdx.x * KPT;
   while (selb != 0) {
     const int j = ctz(selb);
-    if (pos < k) sh.out[pos] = base + j;
+    if (pos < k) emit(pos, base + j);
     ++pos;
     selb &= selb - 1;
   }
+  return min(k, (tot & 0xFFF) + min(tot >> 12, sel.need_eq));
+}
+
+// The selected chunk positions in sh.out[0, k) (-1 past the emitted slots),
+// visible to the whole workgroup on return.
+template <int KPT>
+__device__ void stage_selected(const Keys<KPT>& keys, Selection sel, int k, Shared& sh) {
+  for (int i = threadIdx.x; i < k; i += kThreads) sh.out[i] = -1;   // before the scan's barrier
+  emit_selected(keys, sel, k, sh, [&](int pos, int i) { sh.out[pos] = i; });
   __syncthreads();
 }
 
@@ -447,8 +462,9 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
     load_keys(keys, row, e, lds.stage);
     __syncthreads();   // every wave has read its keys: the staging area is free
     const Selection sel = radix_select(keys, k, sh);
-    stage_selected(keys, sel, k, sh);
-    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = sh.out[i];
+    // positions are the indices here: straight to the output, no staging
+    const int emitted = emit_selected(keys, sel, k, sh, [&](int pos, int i) { out[pos] = i; });
+    for (int i = emitted + (int)threadIdx.x; i < k; i += kThreads) out[i] = -1;
     return;
   }
 

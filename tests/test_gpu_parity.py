@@ -243,6 +243,32 @@ def test_topk_small_bin_ties(dsa, dist, k):
     check_topk(got, host, wl, k)
 
 
+def test_topk_nan_logits_stay_in_range(dsa):
+    """NaN logits give an unspecified selection, but every entry must still be
+    -1 or an index in [0, e_r), ascending and distinct before the -1 padding.
+    The all-ones NaN maps to the excluded key, so the third row has fewer than
+    k orderable keys: exactly those are returned, then -1."""
+    lens = [5000, 40000, 3000]
+    wl = synth.make_workload(lens, [1] * len(lens), 16, seed=37, spare_pages=2)
+    batch, _ = to_dev(wl)
+    rng = np.random.default_rng(5)
+    host = rng.normal(size=(3, 40000)).astype(np.float32)
+    bits = host.view(np.uint32)
+    for pattern, frac in ((0xFFFFFFFF, 0.2), (0x7FC00000, 0.05), (0xFFC00000, 0.05)):
+        mask = rng.random(size=bits.shape) < frac
+        bits[mask] = pattern
+    bits[2, :2000] = 0xFFFFFFFF                       # row 2: 1000 orderable keys at most
+    logits = torch.from_numpy(host).to(DEV)
+    got = run_topk(dsa, batch, logits)
+    for r, e in enumerate(lens):
+        row = got[r]
+        valid = row[row >= 0]
+        assert np.all(row[len(valid):] == -1), f"row {r}: -1 padding is not a suffix"
+        assert np.all(valid < e) and np.all(np.diff(valid) > 0), f"row {r}: out of range or not ascending"
+    orderable = np.nonzero(bits[2, :3000] != 0xFFFFFFFF)[0]
+    assert np.array_equal(got[2, :len(orderable)], orderable) and np.all(got[2, len(orderable):] == -1)
+
+
 def test_topk_ties_from_duplicated_pages(dsa):
     """Every logical block of a sequence maps to the same physical page, so the
     logits repeat every 64 keys: ties broken only by index."""
