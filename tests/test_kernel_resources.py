@@ -11,7 +11,6 @@ import concurrent.futures as cf
 import glob
 import os
 import re
-import shutil
 import subprocess
 
 import pytest
@@ -19,6 +18,13 @@ import pytest
 from sparse_attention_fp8_amd import build
 
 SOURCES = sorted(glob.glob(os.path.join(build.CSRC, "*.hip")))
+
+
+def _have_hipcc():
+    try:
+        return os.path.exists(build.hipcc())
+    except RuntimeError:
+        return False
 
 
 def _resource_remarks(src, out_dir):
@@ -39,8 +45,7 @@ def _resource_remarks(src, out_dir):
     return src, kernels
 
 
-@pytest.mark.skipif(shutil.which(build.hipcc()) is None and not os.path.exists(build.hipcc()),
-                    reason="hipcc not available")
+@pytest.mark.skipif(not _have_hipcc(), reason="hipcc not available")
 def test_no_kernel_spills_vgprs(tmp_path):
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         results = list(ex.map(lambda s: _resource_remarks(s, str(tmp_path)), SOURCES))
