@@ -82,14 +82,20 @@ struct TopkArgs {
 struct Shared {
   // zeroed before a selection (kInitBytes): both histograms and misc
   int hist1[kCopies * kCopyStride + 64];   // + one sink per lane for key 0 (never read)
-  int hist2[kBins + 64];             // + one sink per lane (never read)
+  // out shares hist2's bytes: it is first written after the selection, when
+  // every thread is past the last barrier of the digit searches that read
+  // hist2.  Selection state then takes ~73 KB, so the candidate merges (8 or
+  // 16 keys per thread: no larger staging area) fit two workgroups per CU.
+  union {
+    int hist2[kBins + 64];           // pass two (+ one sink per lane, never read)
+    int out[DSA_MAX_TOPK];           // staged positions
+  };
   int misc[4];
   // the rest is written before it is read
-  int out[DSA_MAX_TOPK];
   int wave_tot[kWaves];
   uint32_t cand[64];                 // keys of a small threshold bin after two digits
 };
-constexpr int kInitBytes = (int)offsetof(Shared, out);
+constexpr int kInitBytes = (int)offsetof(Shared, wave_tot);
 static_assert(kInitBytes % 16 == 0, "zeroed with 16-byte stores");
 
 // The key staging area overlaps the selection state: it is dead once every
@@ -104,6 +110,7 @@ union TopkLds {
   Shared s;
   float4 stage[kThreads * KPT / 4];
 };
+
 
 // Zeroes the part of the selection state in bytes [lo, hi) of the LDS union,
 // with threads tid, tid + nthr, ... of the caller's group.
