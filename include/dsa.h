@@ -111,8 +111,12 @@ typedef struct {
  * the K-side scale applied to the fp32 dot output.)
  *
  *   logits[r, s] = sum_h weights[r, h] * max(q[r, h, :] . k[s, :], 0) * kscale[s]
- *   for 0 <= s < e_r, with q and k decoded from e4m3, the 128-term dots and the
- *   64-term head sum accumulated in fp32.
+ *   for 0 <= s < e_r, with q and k decoded from e4m3 inside fp8 matrix
+ *   instructions.  The products are exact; the matrix unit adds each aligned
+ *   group of 8 of them (dims 8j..8j+7) in a narrow adder (a product 2^14 or
+ *   more below the group's largest may be dropped), the group sums and the
+ *   64-term head sum in fp32 -- errors near 3e-5 of
+ *   sum_h |weights[r, h]| * max(q . k, 0) * kscale[s].
  *
  *  q_fp8         [R, 64, 128] e4m3 codes, 16-byte aligned.  Any q scale must be
  *                folded into `weights` by the caller.
@@ -148,7 +152,9 @@ int dsa_indexer_logits_prefill(const dsa_batch_t* batch, const uint8_t* q_fp8, c
  *  equals +0) go to the lower index.  indices[r, 0:n) = the chosen
  *  n = min(k, e_r) indices in ascending order, indices[r, n:k) = -1.  Only
  *  columns [0, e_r) are read.  NaN logits give an unspecified (but in-range)
- *  selection.
+ *  selection: a NaN either ranks at one end of the order or is never taken
+ *  (negative NaNs with bits at or above 0xFFE00000); a row with fewer than
+ *  min(k, e_r) keys that can be taken returns those, then -1.
  *  logits     [R, logits_stride] fp32, 16-byte aligned, logits_stride % 4 == 0
  *  k          1 <= k <= DSA_MAX_TOPK; rows may hold up to (65536 / k) * 131072
  *             keys (4,194,304 for k = 2048), longer max_seq_len is UNSUPPORTED.

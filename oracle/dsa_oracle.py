@@ -142,22 +142,31 @@ def indexer_logits(q_fp8, weights, idx_cache, block_table, seq_lens, query_start
     logits = np.full((len(row_list), logits_stride), np.nan)
     mag = np.full((len(row_list), logits_stride), np.nan)
     num_pages = np.asarray(idx_cache).shape[0]
+    # The keys of a sequence are decoded once for all of its listed rows (a
+    # row uses the prefix [0, e_r) of them); the arithmetic is per row.
+    keys = {}
     for o, r in enumerate(row_list):
         e = int(ext[r])
         if clean:
             logits[o, e:] = -np.inf
         if e == 0:
             continue
-        page, _ = token_location(bt[seq[r]], np.arange(e))
-        ok = (page >= 0) & (page < num_pages)
+        b = int(seq[r])
+        if b not in keys:
+            e_max = max(int(ext[x]) for x in row_list if seq[x] == b)
+            page, _ = token_location(bt[b], np.arange(e_max))
+            ok_b = (page >= 0) & (page < num_pages)
+            s_b = np.nonzero(ok_b)[0]
+            codes, scales_b = indexer_keys(idx_cache, bt[b], s_b)
+            keys[b] = (s_b, e4m3fn_decode(codes), scales_b)
+        s_b, K_b, scales_b = keys[b]
+        n = int(np.searchsorted(s_b, e))       # the in-range tokens below e_r
         logits[o, :e] = -np.inf                # tokens on an out-of-range page stay masked
         mag[o, :e] = 0.0
-        if not ok.any():
+        if n == 0:
             continue
-        s = np.nonzero(ok)[0]
-        codes, scales = indexer_keys(idx_cache, bt[seq[r]], s)
+        s, K, scales = s_b[:n], K_b[:n], scales_b[:n]
         Q = e4m3fn_decode(q_fp8[r])            # [64, 128]
-        K = e4m3fn_decode(codes)               # [n, 128]
         relu = np.maximum(Q @ K.T, 0.0)        # [64, n]
         logits[o, s] = (w[r] @ relu) * scales
         mag[o, s] = (np.abs(w[r]) @ relu) * scales

@@ -166,8 +166,9 @@ __device__ __forceinline__ int block_scan(int v, Shared& sh) {
 }
 
 // Keys [t*KPT, (t+1)*KPT) of thread t from src[0, n).  Positions >= n get key
-// 0: every finite float and +-inf maps to a key >= 2^21, so with n > k valid
-// keys the k-th largest key is never 0 and a key-0 slot is never selected.
+// 0.  Every finite float and +-inf maps to a key >= 2^21; keys below 2^21 (key
+// 0, and the negative NaNs whose bits are at or above 0xFFE00000) are not
+// orderable: the selection counts them nowhere and never takes them.
 // Wave w copies the V = KPT / 4 float4s of each of its lanes to LDS: owner
 // lane L's float4 j goes to slot L V + (j ^ swz(L)) of the wave's area, with
 // swz(L) = (L / (16 / V)) % V.  The 16 lanes a 128-bit LDS read serves per
@@ -281,10 +282,11 @@ __device__ __forceinline__ void find_digit(const int* hist, int rem, Shared& sh)
   __syncthreads();
 }
 
-// Exact selection of the k largest of the n valid keys (n > k >= 1).
-// Key 0 (an out-of-range slot) is counted nowhere, and every prefix and
-// threshold below is at least 2^21 - 1 (the threshold bin holds a valid key),
-// so the later comparisons exclude key 0 by themselves.
+// Exact selection of the k largest orderable keys (keys >= 2^21) of the n
+// valid keys (n > k >= 1).  Keys below 2^21 (an out-of-range slot is key 0) go
+// to pass one's sink, so the threshold digit is never 0 and every prefix and
+// threshold below is at least 2^21 - 1: the later comparisons exclude those
+// keys by themselves.
 //  pass 1: 11-bit top digit of every key;
 //  passes 2 and 3 (11 and 10 bits) scan the registers again and count only
 //  the keys whose higher digits match the prefix found so far.  (Compacting
@@ -339,14 +341,14 @@ __device__ Selection resolve_small_bin(const Keys<KPT>& keys, uint32_t prefix, u
 template <int KPT>
 __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   const int l = lane_id();
-  // Key 0 counts into a per-lane sink past the bins instead of branching
-  // around the atomic: a branch per key costs more than the select.
+  // Keys below 2^21 count into a per-lane sink past the bins instead of
+  // branching around the atomic: a branch per key costs more than the select.
   const int copy = l & (kCopies - 1);
   const int sink = kCopies * kCopyStride + l;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const uint32_t key = keys.v[j];
-    const int addr = key != 0u ? copy * kCopyStride + (int)(key >> 21) : sink;
+    const int addr = key >= (1u << 21) ? copy * kCopyStride + (int)(key >> 21) : sink;
     __hip_atomic_fetch_add(&sh.hist1[addr], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();
@@ -354,9 +356,8 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
   uint32_t prefix = (uint32_t)sh.misc[0] << 21;
   int rem = k - sh.misc[1];
   const int in_bin = sh.misc[2];
-  // No crossing: fewer than k keys are orderable (key 0 -- an out-of-range
-  // slot, or the all-ones NaN -- counts nowhere).  Take all of them.
-  if (in_bin == 0) return Selection{0u, 0};
+  // No crossing: fewer than k keys are orderable.  Take all of them.
+  if (in_bin == 0) return Selection{(1u << 21) - 1u, 0};
   if (rem == in_bin) return Selection{prefix - 1u, 0};  // the whole bin is taken
 
   // pass three counts into hist1's first kBins entries
@@ -398,7 +399,7 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
 // set bits of the combined mask in order.  Out-of-range slots (key 0) are
 // never taken and slots are clamped to k.  Returns how many slots were
 // emitted: slots [0, that) each exactly once -- k, unless the row holds fewer
-// than k orderable keys (a float whose key is 0, such as the all-ones NaN).
+// than k orderable keys (some NaNs are not orderable, see load_keys).
 template <int KPT, class Emit>
 __device__ int emit_selected(const Keys<KPT>& keys, Selection sel, int k, Shared& sh, Emit emit) {
   MaskT<KPT> gtb = 0, eqb = 0;

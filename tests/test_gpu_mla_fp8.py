@@ -98,6 +98,19 @@ def test_sparse_mla_fp8_parity(dsa, H, splits):
     check_mla(out, lse, o_ref, l_ref, f"fp8 H={H} splits={splits}")
 
 
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 16])
+@pytest.mark.parametrize("k", [1, 100, 2047])
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_sparse_mla_fp8_parity_other_k(dsa, H, k, splits):
+    """k below the 2048 maximum over the fp8 latent cache: a partial last
+    tile, fewer tiles per split, rows with fewer keys than k."""
+    wl, batch, t, kv8, idx = mla8_inputs([3000, 700, 130, 2049, 40], [1, 2, 1, 1, 1], H,
+                                         seed=7 * k + H + splits, k=k)
+    out, lse = run_mla8(dsa, wl, batch, t, idx, splits)
+    o_ref, l_ref = mla8_oracle(wl, kv8, idx)
+    check_mla(out, lse, o_ref, l_ref, f"fp8 H={H} k={k} splits={splits}")
+
+
 def test_sparse_mla_fp8_padded_pages_masked_and_empty_rows(dsa):
     wl, batch, t, kv8, idx = mla8_inputs([5000, 600, 64], [1, 2, 1], 16, seed=78,
                                          stride=oracle.KV8_PAGE_BYTES + 128)

@@ -123,11 +123,14 @@ def test_indexer_hand_worked(stride):
     q, w, cache, bt, sl, qs = _gold_indexer_inputs(stride)
     logits, mag, ext = oracle.indexer_logits(q, w, cache, bt, sl, qs, logits_stride=4, clean=True)
     exp = GOLD["indexer"]["expected_logits"]
+    exp_mag = GOLD["indexer"]["expected_magnitudes"]
     for r in range(2):
         want = [float(v) for v in exp[str(r)]]
         got = logits[r, :3].tolist()
         assert got == want, (r, got, want)
         assert logits[r, 3] == -np.inf
+        want_mag = [float(v) for v in exp_mag[str(r)]]
+        assert mag[r, :len(want_mag)].tolist() == want_mag, (r, mag[r, :3], want_mag)
     assert ext.tolist() == [2, 3]
 
 
@@ -138,16 +141,21 @@ def test_indexer_dirty_leaves_tail_unwritten():
 
 
 def _brute_logit(q_codes, w, k_codes, k_scale):
-    """Pure-Python loops over heads and dims; values from torch's fp8 conversion."""
+    """Pure-Python loops over heads and dims; values from torch's fp8 conversion.
+    Returns (logit, magnitude): the head sum with w_h, and the same sum with
+    |w_h| (the scale of the logits tolerance), each times the K scale."""
     qv = fp8_lib(q_codes)
     kv = fp8_lib(k_codes)
     total = 0.0
+    size = 0.0
     for h in range(64):
         dot = 0.0
         for d in range(128):
             dot += float(qv[h, d]) * float(kv[d])
-        total += float(w[h]) * (dot if dot > 0.0 else 0.0)
-    return total * float(k_scale)
+        relu = dot if dot > 0.0 else 0.0
+        total += float(w[h]) * relu
+        size += abs(float(w[h])) * relu
+    return total * float(k_scale), size * float(k_scale)
 
 
 def test_indexer_matches_brute_force_loops():
@@ -164,8 +172,11 @@ def test_indexer_matches_brute_force_loops():
             p, slot = bt[seq[r], s // 64], s % 64
             kc = cache[p, slot * 128:(slot + 1) * 128]
             ks = cache[p, 8192 + 4 * slot:8192 + 4 * slot + 4].view(np.float32)[0]
-            want = _brute_logit(wl.q_fp8.numpy()[r], wl.weights.numpy()[r], kc, ks)
-            assert abs(logits[r, s] - want) <= 1e-12 * max(1.0, mag[r, s]), (r, s)
+            want, want_mag = _brute_logit(wl.q_fp8.numpy()[r], wl.weights.numpy()[r], kc, ks)
+            # both tolerances scale with the loops' own magnitude, not the oracle's
+            assert abs(logits[r, s] - want) <= 1e-12 * max(1.0, want_mag), (r, s)
+            assert abs(mag[r, s] - want_mag) <= 1e-12 * max(1.0, want_mag), (r, s)
+            assert want_mag >= abs(want)
         assert np.all(np.isneginf(logits[r, ext[r]:]))
     assert np.isfinite(logits[0, :ext[0]]).all()
 
@@ -186,12 +197,18 @@ def test_indexer_one_hot_and_signed_pair_give_k_times_scale():
         q = np.zeros((1, 64, 128), np.uint8)
         w = np.zeros((1, 64), np.float32)
         q[0, 5, d], w[0, 5] = 0x38, 1.0            # +1.0
-        lg1, _, _ = oracle.indexer_logits(q, w, cache, bt, [L], [0, 1], L)
+        lg1, mag1, _ = oracle.indexer_logits(q, w, cache, bt, [L], [0, 1], L)
         kd = fp8_lib(codes[:, d]) * scales.astype(np.float64)
         assert np.array_equal(lg1[0], np.maximum(kd, 0.0))
+        assert np.array_equal(mag1[0], np.maximum(kd, 0.0))      # w = +1: magnitude = logit
         q[0, 9, d], w[0, 9] = 0xB8, -1.0           # -1.0
-        lg2, _, _ = oracle.indexer_logits(q, w, cache, bt, [L], [0, 1], L)
+        lg2, mag2, _ = oracle.indexer_logits(q, w, cache, bt, [L], [0, 1], L)
         assert np.array_equal(lg2[0], kd)
+        # relu(k_d) from the +1 head and relu(-k_d) from the -1 head add up to |k_d|
+        assert np.array_equal(mag2[0], np.abs(kd))
+        w[0, 9] = -3.0                             # |w| scales its head's share
+        _, mag3, _ = oracle.indexer_logits(q, w, cache, bt, [L], [0, 1], L)
+        assert np.array_equal(mag3[0], np.maximum(kd, 0.0) + 3.0 * np.maximum(-kd, 0.0))
 
 
 def test_indexer_all_negative_dots_give_zero():
@@ -202,6 +219,23 @@ def test_indexer_all_negative_dots_give_zero():
     w = np.random.default_rng(1).normal(size=(1, 64)).astype(np.float32)
     lg, mag, _ = oracle.indexer_logits(q, w, cache, np.array([[0]]), [L], [0, 1], L)
     assert np.array_equal(lg[0], np.zeros(L)) and np.array_equal(mag[0], np.zeros(L))
+
+
+def test_indexer_magnitude_bounds_and_same_sign_weights():
+    """magnitude >= |logit| everywhere; with every weight >= 0 it equals the
+    logit, with every weight <= 0 it equals -logit (closed forms of |w|)."""
+    wl = synth.make_workload([300, 70], [2, 1], 16, seed=13, spare_pages=2)
+    q8, w = wl.q_fp8.numpy(), wl.weights.numpy()
+    rest = (wl.idx_cache.numpy(), wl.block_table.numpy(), wl.seq_lens.numpy(), wl.query_start.numpy(), 304)
+    lg, mag, _ = oracle.indexer_logits(q8, w, *rest)
+    fin = np.isfinite(lg)
+    assert np.all(mag[fin] >= np.abs(lg[fin]))
+    assert np.any(mag[fin] > np.abs(lg[fin]) * (1 + 1e-6))   # mixed-sign weights cancel somewhere
+    for sign in (1.0, -1.0):
+        ws = (sign * np.abs(w)).astype(np.float32)
+        lg_s, mag_s, _ = oracle.indexer_logits(q8, ws, *rest)
+        assert np.allclose(sign * lg_s[fin], mag_s[fin], rtol=1e-15, atol=0)
+        assert np.array_equal(mag_s[fin], mag[fin])      # magnitude ignores the weights' signs
 
 
 def test_indexer_page_permutation_invariance():
