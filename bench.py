@@ -11,8 +11,11 @@ timed region replays a HIP graph holding one step per cache copy back to back
 paid once per `copies` steps); the one-graph-per-step rate is reported beside
 it.
 
-Prints one JSON line (metric, value = steps/s, roofline of the dominant kernel,
-the float64 oracle timed on the host as cpu_baseline).
+Prints one JSON line: metric, value = steps/s of the headline workload (by
+default c5, MTP decode over 64 sequences at 128 MLA heads: the largest decode
+workload one GPU takes), the roofline of its dominant kernel, the other decode
+workloads of the same run under "also" (by default c2), and the float64 oracle
+timed on the host, stage by stage, as cpu_baseline.
 """
 from __future__ import annotations
 
@@ -39,7 +42,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "x1m"])
+    ap.add_argument("--config", default="c5", choices=["c1", "c2", "c3", "c4", "c5", "x1m"],
+                    help="headline workload (default c5: the largest single-GPU decode workload)")
+    ap.add_argument("--also", default="c2",
+                    help="comma-separated workloads measured after the headline in the same run and reported "
+                         "under 'also' (empty: none)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate through (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -111,14 +118,26 @@ def measured_traffic(config, stage):
     return None
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s):
-    """Time the float64 oracle on a bounded, seeded sample of the step's rows."""
+    """Time the float64 oracle on a bounded, seeded sample of the step's rows,
+    stage by stage (indexer logits, top-k, sparse MLA), scaled to whole steps."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        blas_threads = 1
     R = wl.num_rows
     rng = np.random.default_rng(0)
     order = rng.permutation(R)
@@ -129,29 +148,42 @@ def cpu_baseline(wl, budget_s):
     # Rows in a seeded order until the budget runs out; a step that finishes
     # early is repeated until at least half the budget is spent, so the
     # figure averages over several seconds of work.
+    stage_s = {"indexer": 0.0, "topk": 0.0, "sparse_mla": 0.0}
     done, passes, t0 = 0, 0, time.perf_counter()
     out_of_time = False
     while not out_of_time:
         for r in order:
+            t1 = time.perf_counter()
             lg, _, _ = oracle.indexer_logits(q8, w, cache, bt, sl, qs, stride, rows=[int(r)])
+            t2 = time.perf_counter()
             idx = oracle.topk(lg, sl, qs, wl.topk, rows=[int(r)])
+            t3 = time.perf_counter()
             oracle.sparse_mla(qm, kv, bt, sl, qs, idx, wl.softmax_scale, rows=[int(r)])
+            t4 = time.perf_counter()
+            stage_s["indexer"] += t2 - t1
+            stage_s["topk"] += t3 - t2
+            stage_s["sparse_mla"] += t4 - t3
             done += 1
-            if time.perf_counter() - t0 > budget_s:
+            if t4 - t0 > budget_s:
                 out_of_time = True
                 break
         else:
             passes += 1
             out_of_time = time.perf_counter() - t0 > budget_s / 2
     dt = time.perf_counter() - t0
-    steps_per_s = (done / R) / dt
+    steps = done / R
     if passes >= 1:
         sample = (f"{passes} whole step(s) plus {done - passes * R} rows, {done} rows in all "
                   f"(indexer+top-k+sparse MLA per row, float64 numpy), {dt:.1f} s")
     else:
         sample = (f"{done} of {R} rows of one step (indexer+top-k+sparse MLA per row, float64 numpy), "
                   f"{dt:.1f} s, scaled by {R}/{done}")
-    return {"value": steps_per_s, "unit": "steps/s", "cores": int(cores), "kind": "oracle", "sample": sample}
+    return {"value": steps / dt, "unit": "steps/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": sample,
+            "stage_s_per_step": {k: v / steps for k, v in stage_s.items()},
+            "threads_note": "cores = the BLAS pool's threads (the matrix products); the rest of the oracle "
+                            "runs on one thread",
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
 def pre_path(dsa, wl, batch_dev, base, dev, steps):
@@ -215,17 +247,11 @@ def pre_path(dsa, wl, batch_dev, base, dev, steps):
     return res
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
-        sys.exit(2)
-    import sparse_attention_fp8_amd as dsa
-    from sparse_attention_fp8_amd import synth
-
-    dsa.load()
+def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True):
+    """Times one workload's step (and each stage) from HIP graph replays.
+    Returns the figures of one JSON line (without the CPU baseline)."""
     dev = torch.device("cuda:0")
-    wl = synth.make_config(args.config, args.seed)
+    wl = synth.make_config(name, seed)
     R, H, k = wl.num_rows, wl.num_heads, wl.topk
     prefill = wl.max_q_len > 2
     nbytes = algorithmic_bytes(wl)
@@ -252,31 +278,32 @@ def main():
     out = torch.empty(R, H, 512, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(R, H, dtype=torch.float32, device=dev)
     ws_topk = torch.empty(max(dsa.topk_workspace_bytes(batch, k), 1), dtype=torch.uint8, device=dev)
-    ws_mla = torch.empty(max(dsa.sparse_mla_workspace_bytes(batch, H, k, args.splits), 1), dtype=torch.uint8,
+    ws_mla = torch.empty(max(dsa.sparse_mla_workspace_bytes(batch, H, k, splits), 1), dtype=torch.uint8,
                          device=dev)
-    splits = args.splits or dsa.sparse_mla_pick_splits(batch, H, k)
+    nsplits = splits or dsa.sparse_mla_pick_splits(batch, H, k)
     indexer = dsa.indexer_logits_prefill if prefill else dsa.indexer_logits_paged
 
-    def run_stage(name, i):
+    def run_stage(stage, i):
         t = sets[i % copies]
-        if name == "indexer":
+        if stage == "indexer":
             indexer(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=False)
-        elif name == "topk":
+        elif stage == "topk":
             dsa.topk(batch, logits, indices, k=k, workspace=ws_topk)
-        elif name == "sparse_mla_fp8":
+        elif stage == "sparse_mla_fp8":
             dsa.sparse_mla_decode_fp8(batch, t["q_mla"], t["kv8"], indices, wl.softmax_scale, out, lse,
-                                      num_splits=args.splits, workspace=ws_mla)
+                                      num_splits=splits, workspace=ws_mla)
         else:
             dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
-                                  num_splits=args.splits, workspace=ws_mla)
+                                  num_splits=splits, workspace=ws_mla)
 
-    mla_stage = "sparse_mla_fp8" if args.kv == "fp8" else "sparse_mla"
+    mla_stage = "sparse_mla_fp8" if kv == "fp8" else "sparse_mla"
     stages = ("indexer", "topk", mla_stage)
-    other_mla = "sparse_mla" if args.kv == "fp8" else "sparse_mla_fp8"
+    other_mla = "sparse_mla" if kv == "fp8" else "sparse_mla_fp8"
+    timed_stages = stages + ((other_mla,) if details else ())
 
     def step(i):
-        for name in stages:
-            run_stage(name, i)
+        for stage in stages:
+            run_stage(stage, i)
 
     # eager warm-up (also loads every code object before capture)
     for i in range(max(args.warmup, 1)):
@@ -300,12 +327,12 @@ def main():
     # the stage's average launch duration is measured on its own stream.
     reps = 2 * copies
     stage_graphs = {}
-    for name in stages + (other_mla,):
+    for stage in timed_stages:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(reps):
-                run_stage(name, i)
-        stage_graphs[name] = g
+                run_stage(stage, i)
+        stage_graphs[stage] = g
     torch.cuda.synchronize()
     for i in range(args.warmup):
         step_graphs[i % copies].replay()
@@ -333,17 +360,59 @@ def main():
 
     stage_ms = {}
     stage_rounds = max(1, args.steps // reps)
-    for name in stages + (other_mla,):
-        stage_graphs[name].replay()
+    for stage in timed_stages:
+        stage_graphs[stage].replay()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(stage_rounds):
-            stage_graphs[name].replay()
+            stage_graphs[stage].replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        stage_ms[name] = e0.elapsed_time(e1) / (stage_rounds * reps)
+        stage_ms[stage] = e0.elapsed_time(e1) / (stage_rounds * reps)
 
-    # device-to-device copy rate of the same run (1 GiB), for reference
+    alt_ms = stage_ms.pop(other_mla) if details else None
+    total_bytes = nbytes["indexer"] + nbytes["topk"] + nbytes[mla_stage]
+    if prefill:
+        dom = "indexer"
+        achieved = nbytes["indexer_flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": measured_traffic(name, "indexer_prefill"),
+                "kernel": "indexer_prefill", "per_launch": f"{nbytes['indexer_flops']} flop"}
+    else:
+        dom = max(stage_ms, key=stage_ms.get)
+        achieved = nbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(name, dom), "kernel": dom,
+                "per_launch": f"{nbytes[dom]} B"}
+    res = {
+        "ms": ms, "ms_graph_each": ms_graph_each, "stage_ms": stage_ms, "roofline": roof,
+        "step_bytes": total_bytes, "step_hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "stage_hbm_frac": {st: nbytes[st] / (stage_ms[st] * 1e-3) / 1e9 / HBM_PEAK_GBS for st in stages},
+        "mla_mfma_frac": nbytes["mla_flops"] / (stage_ms[mla_stage] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "config": {"workload": synth.CONFIGS[name], "name": name, "rows": R, "mla_heads": H,
+                   "topk": k, "splits": nsplits, "cache_copies": copies,
+                   "seed": seed if seed is not None else synth.DEFAULT_SEEDS[name]},
+        "timing": f"HIP graph replays: a graph of {copies} steps (one per cache copy) replayed "
+                  f"{args.steps // copies} times plus {args.steps % copies} single-step graphs; stage times from "
+                  f"graphs of {reps} launches of one entry point",
+        "rows": R,
+    }
+    if details:
+        res["other_kv_stage"] = {"stage": other_mla, "us": alt_ms * 1e3, "bytes": nbytes[other_mla],
+                                 "GBps": nbytes[other_mla] / (alt_ms * 1e-3) / 1e9,
+                                 "hbm_frac": nbytes[other_mla] / (alt_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "note": "the same indices through the other latent-cache format"}
+        res["pre_path"] = pre_path(dsa, wl, batch, base, dev, args.steps)
+        res["wl"] = wl
+    del sets, base
+    torch.cuda.synchronize()
+    return res
+
+
+def copy_rate_gbs():
+    """Device-to-device copy rate of this run (1 GiB), for reference."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
     cbuf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cdst = torch.empty_like(cbuf)
     cdst.copy_(cbuf)
@@ -353,23 +422,21 @@ def main():
         cdst.copy_(cbuf)
     e1.record(stream)
     torch.cuda.synchronize()
-    copy_gbs = 5 * 2 * cbuf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del cbuf, cdst
+    return 5 * 2 * cbuf.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
-    alt_ms = stage_ms.pop(other_mla)
-    total_bytes = nbytes["indexer"] + nbytes["topk"] + nbytes[mla_stage]
-    if prefill:
-        dom = "indexer"
-        achieved = nbytes["indexer_flops"] / (stage_ms[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP8_PEAK_TFLOPS, "traffic": measured_traffic(args.config, "indexer_prefill"),
-                "kernel": "indexer_prefill", "per_launch": f"{nbytes['indexer_flops']} flop"}
-    else:
-        dom = max(stage_ms, key=stage_ms.get)
-        achieved = nbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, dom), "kernel": dom,
-                "per_launch": f"{nbytes[dom]} B"}
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import sparse_attention_fp8_amd as dsa
+    from sparse_attention_fp8_amd import synth
+
+    dsa.load()
+    head = measure(dsa, synth, args.config, args, kv=args.kv, splits=args.splits, seed=args.seed)
+    copy_gbs = copy_rate_gbs()
+    ms = head["ms"]
     line = {
         "metric": "DSA decode steps/s (indexer+topk+sparse MLA) and % of HBM roofline at 1 GPU",
         "kv_cache": args.kv,
@@ -385,25 +452,33 @@ def main():
         "dtype": "fp8 indexer / bf16 MLA, fp32 accumulate" if args.kv == "bf16"
                  else "fp8 indexer / fp8-cache MLA (bf16 operands), fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": synth.CONFIGS[args.config], "name": args.config, "rows": R, "mla_heads": H,
-                   "topk": k, "splits": splits, "cache_copies": copies,
-                   "seed": args.seed if args.seed is not None else synth.DEFAULT_SEEDS[args.config]},
-        "roofline": roof,
-        "stages_ms": stage_ms,
-        "step_bytes": total_bytes,
-        "step_hbm_frac": total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "stages_ms": head["stage_ms"],
+        "stage_hbm_frac": head["stage_hbm_frac"],
+        "mla_mfma_frac": head["mla_mfma_frac"],
+        "step_bytes": head["step_bytes"],
+        "step_hbm_frac": head["step_hbm_frac"],
         "copy_GBps": copy_gbs,
-        "timing": f"HIP graph replays: a graph of {copies} steps (one per cache copy) replayed "
-                  f"{args.steps // copies} times plus {args.steps % copies} single-step graphs; stage times from "
-                  f"graphs of {reps} launches of one entry point",
-        "ms_per_step_one_graph_each": ms_graph_each,
-        "rows_per_s": R * 1000.0 / ms,
+        "timing": head["timing"],
+        "ms_per_step_one_graph_each": head["ms_graph_each"],
+        "rows_per_s": head["rows"] * 1000.0 / ms,
+        "other_kv_stage": head["other_kv_stage"],
+        "pre_path": head["pre_path"],
     }
-    line["other_kv_stage"] = {"stage": other_mla, "us": alt_ms * 1e3, "bytes": nbytes[other_mla],
-                              "GBps": nbytes[other_mla] / (alt_ms * 1e-3) / 1e9,
-                              "hbm_frac": nbytes[other_mla] / (alt_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              "note": "the same indices through the other latent-cache format"}
-    line["pre_path"] = pre_path(dsa, wl, batch, base, dev, args.steps)
+    wl = head.pop("wl")
+    del head
+    # the other decode workloads, measured in the same run (same timing method)
+    extra = {}
+    for name in [x for x in args.also.split(",") if x and x != args.config]:
+        r = measure(dsa, synth, name, args, kv=args.kv, details=False)
+        extra[name] = {"workload": r["config"]["workload"], "ms_per_step": r["ms"], "steps_per_s": 1000.0 / r["ms"],
+                       "stages_ms": r["stage_ms"], "step_bytes": r["step_bytes"],
+                       "step_hbm_frac": r["step_hbm_frac"], "stage_hbm_frac": r["stage_hbm_frac"],
+                       "roofline": r["roofline"], "splits": r["config"]["splits"],
+                       "ms_per_step_one_graph_each": r["ms_graph_each"]}
+    if extra:
+        line["also"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
     print(json.dumps(line), flush=True)
