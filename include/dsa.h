@@ -181,7 +181,8 @@ int dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_strid
  *     out[r, h, :] = sum_s softmax(z)_s * c_s[0:512]      (bf16, round to nearest even)
  *     lse[r, h]    = ln sum_s exp(z_s)                     (fp32; -inf, out = 0 if none valid)
  *  q           [R, H, 576] bf16, 16-byte aligned
- *  num_heads   H: 16, 32, or a multiple of 64
+ *  num_heads   H: a multiple of 16 from 16 to 1024 (one GPU's share of the
+ *              MLA heads: 16 of 128 at TP = 8 ... all 128 at TP = 1)
  *  kv_cache    latent pages, 16-byte aligned; kv_page_stride in elements
  *  indices     [R, k] int32 logical token ids (typically dsa_topk's output)
  *  k           1 <= k <= DSA_MAX_TOPK

@@ -177,7 +177,7 @@ int dsa_topk(const dsa_batch_t* batch, const float* logits, int64_t logits_strid
                     "dsa_topk launch");
 }
 
-static bool heads_supported(int32_t H) { return H == 16 || H == 32 || (H >= 64 && H % 64 == 0 && H <= 1024); }
+static bool heads_supported(int32_t H) { return H >= 16 && H <= 1024 && H % 16 == 0; }
 
 int32_t dsa_sparse_mla_pick_splits(const dsa_batch_t* batch, int32_t num_heads, int32_t k) {
   if (!batch || !heads_supported(num_heads) || k < 1 || k > DSA_MAX_TOPK) return 1;
@@ -198,7 +198,7 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
   int st = check_batch(batch);
   if (st != DSA_OK) return st;
   if (!heads_supported(num_heads))
-    return fail(DSA_ERR_UNSUPPORTED, "num_heads=%d: supported are 16, 32 and multiples of 64 up to 1024", num_heads);
+    return fail(DSA_ERR_UNSUPPORTED, "num_heads=%d: supported are multiples of 16 from 16 to 1024", num_heads);
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k=%d outside [1, %d]", k, DSA_MAX_TOPK);
   if (kv_page_stride < (int64_t)DSA_PAGE_SIZE * DSA_KV_DIM || kv_page_stride % 8 != 0)
     return fail(DSA_ERR_INVALID, "kv_page_stride=%lld must be >= 36864 elements and a multiple of 8",
@@ -233,7 +233,7 @@ int dsa_sparse_mla_decode_fp8(const dsa_batch_t* batch, const uint16_t* q, int32
   int st = check_batch(batch);
   if (st != DSA_OK) return st;
   if (!heads_supported(num_heads))
-    return fail(DSA_ERR_UNSUPPORTED, "num_heads=%d: supported are 16, 32 and multiples of 64 up to 1024", num_heads);
+    return fail(DSA_ERR_UNSUPPORTED, "num_heads=%d: supported are multiples of 16 from 16 to 1024", num_heads);
   if (k < 1 || k > DSA_MAX_TOPK) return fail(DSA_ERR_UNSUPPORTED, "k=%d outside [1, %d]", k, DSA_MAX_TOPK);
   if (kv_page_stride_bytes < DSA_KV8_PAGE_BYTES || kv_page_stride_bytes % 16 != 0)
     return fail(DSA_ERR_INVALID, "kv_page_stride_bytes=%lld must be >= %d and a multiple of 16",

@@ -13,8 +13,12 @@
 //      16 heads:  4 waves, each scores 16 of the tile's 64 tokens and
 //                 accumulates 128 of the 512 output dims;
 //      32 heads:  4 waves = 2 head tiles x 2 parts (32 tokens / 256 dims each);
-//      >=64 heads: 8 waves = 4 head tiles x 2 parts, 64-head blocks; in PV
-//      each wave instead takes two head tiles over 128 dims.
+//      >=48 heads: 8 waves = 4 head tiles x 2 parts, 64-head blocks; in PV
+//      each wave instead takes two head tiles over 128 dims.  When H is not a
+//      multiple of 64 the last block holds H % 64 heads: its missing head
+//      tiles score the block's first head tile and store nothing (the same
+//      instruction stream as a full block: a branch inside the tile loop
+//      costs every head count a fifth of its speed).
 //    Scores of a head tile are computed once; the tile maxima and the bf16
 //    probabilities are exchanged through LDS between the waves, and every
 //    wave accumulates its own (heads, dims) block over all 64 tokens.
@@ -121,6 +125,10 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   const int h = hb * (16 * HT) + ht * 16 + n16;
   const int hgp = wave % HGP, dpart = wave / HGP;
   const int hp0 = hb * (16 * HT) + hgp * (16 * PVH) + n16;
+  // Head tiles of this block that exist (a last block of H % 64 heads has
+  // fewer; its tile 0 always does).  A missing tile is scored with the q of
+  // the block's first tile and its results are not stored.  Wave-uniform.
+  const int hq = hb * (16 * HT) + ht * 16 < a.H ? h : hb * (16 * HT) + n16;
   const int d_base = dpart * DW;
 
   const int slot0 = sp * a.split_slots;
@@ -187,7 +195,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   // Q^T operand: lane supplies head h, dims 32*ks + 8*g .. +8.
   uint4 qreg[18];
   {
-    const uint16_t* qp = a.q + ((int64_t)r * a.H + h) * kKvDim + 8 * g;
+    const uint16_t* qp = a.q + ((int64_t)r * a.H + hq) * kKvDim + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
   }
@@ -415,6 +423,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 #pragma unroll
     for (int pp = 0; pp < TP; ++pp) l_tot += sh.tmax[hgp * PVH + hh][pp][n16];
     const int hp = hp0 + 16 * hh;
+    if (hp - n16 >= a.H) continue;                    // a missing head tile
     if (a.splits == 1) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
       uint16_t* op = a.out + ((int64_t)r * a.H + hp) * kVDim + d_base + 4 * g;
@@ -448,7 +457,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 
 MlaPlan plan_sparse_mla(int num_rows, int max_seq_len, int H, int k, int num_splits, int num_cus) {
   MlaPlan p{};
-  const int head_blocks = H <= 32 ? 1 : H / 64;   // 16-, 32- or 64-head workgroups
+  const int head_blocks = H <= 32 ? 1 : (H + 63) / 64;   // 16-, 32- or 64-head workgroups
   const int live = max(1, min(k, max(max_seq_len, 1)));
   const int tiles = (live + kTile - 1) / kTile;      // tiles that can hold valid entries
   const int all_tiles = (k + kTile - 1) / kTile;

@@ -139,6 +139,13 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   const int ht = wave % HT, part = wave / HT;
   const int h = hb * (16 * HT) + ht * 16 + n16;
   const int d_base = part * DW;
+  // Whether this wave's head tile exists (a last block of H % 64 heads has
+  // fewer; its tile 0 always does).  A missing tile is scored with the q of
+  // the block's first tile and its results are not stored: the same
+  // instruction stream as a full block (a branch inside the tile loop costs
+  // registers and speed at every head count).  Wave-uniform.
+  const bool on = hb * (16 * HT) + ht * 16 < a.H;
+  const int hq = on ? h : hb * (16 * HT) + n16;
   const int slot0 = sp * a.split_slots;
   const int slot1 = min(slot0 + a.split_slots, a.k);
   const int ntiles = (slot1 - slot0 + kTile8 - 1) / kTile8;
@@ -148,7 +155,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   // 64 j + 16 g + 0..7, MFMA 2 j + 1 dims 64 j + 16 g + 8..15 (the k order the
   // 128-bit code reads deliver).  Rope step s: dims 512 + 32 s + 8 g + 0..7.
   {
-    const uint16_t* qp = a.q + ((int64_t)r * a.H + h) * kKvDim;
+    const uint16_t* qp = a.q + ((int64_t)r * a.H + hq) * kKvDim;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       qreg[2 * j] = *reinterpret_cast<const uint4*>(qp + 64 * j + 16 * g);
@@ -420,6 +427,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   asm volatile("" : "+v"(ln));
   const int ho = hb * (16 * HT) + ht * 16 + (ln & 15);   // = h
   const int go = ln >> 4;                                  // = g
+  if (!on) return;
   if (a.splits == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* op = a.out + ((int64_t)r * a.H + ho) * kVDim + d_base + 4 * go;

@@ -139,8 +139,13 @@ def mla_call(lib, b, H=16, k=2048, splits=0, ws=FAKE, ws_bytes=1 << 40, **kw):
 
 def test_sparse_mla_argument_checks(lib):
     assert mla_call(lib, None) == ERR_NULL
-    for H in (0, 8, 48, 96, 100):
+    for H in (0, 8, 24, 100, 1040, -16):
         assert mla_call(lib, batch(), H=H) == ERR_UNSUPPORTED, H
+    # every multiple of 16 up to 128 (one GPU's share of the heads) is accepted;
+    # with no rows nothing is launched
+    for H in range(16, 129, 16):
+        assert mla_call(lib, batch(num_rows=0), H=H) == OK, H
+        assert lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(batch(num_rows=1)), H, 2048, 0) > 0, H
     assert mla_call(lib, batch(), k=0) == ERR_UNSUPPORTED
     assert mla_call(lib, batch(), k=4096) == ERR_UNSUPPORTED
     assert mla_call(lib, batch(), kv_stride=64 * 576 - 8) == ERR_INVALID
@@ -166,6 +171,8 @@ def test_split_heuristic_and_workspace(lib):
     assert splits(4096, 65536, 16) == 1         # prefill-sized batch: single pass
     assert splits(1, 100, 16) == 2              # never more splits than tiles holding keys
     assert 1 <= splits(128, 65536, 128) <= 4
+    # a last 64-head block of H % 64 heads counts as a block of its own
+    assert splits(1, 4096, 112) == splits(1, 4096, 128) and splits(1, 4096, 80) == splits(1, 4096, 128)
     # one split needs no workspace
     b = batch(num_rows=4096, max_seq_len=65536, bt_stride=1024)
     assert lib.dsa_sparse_mla_workspace_bytes(ctypes.byref(b), 16, 2048, 1) == 0
@@ -249,7 +256,7 @@ def test_fp8_latent_entries_reject_bad_arguments(lib):
     assert call(args(stride=41968)) == ERR_INVALID
     assert b"kv_page_stride_bytes" in lib.dsa_last_error_message()
     assert call(args(stride=41984 + 8)) == ERR_INVALID
-    assert call(args(H=48)) == ERR_UNSUPPORTED
+    assert call(args(H=24)) == ERR_UNSUPPORTED
     assert call(args(kv=None)) == ERR_NULL
     assert call(args(kv=FAKE + 8)) == ERR_INVALID
     assert call(args(sp=4)) == ERR_WORKSPACE                   # split partials need a workspace

@@ -405,7 +405,7 @@ def run_mla(dsa, wl, batch, t, idx, splits):
 
 
 @pytest.mark.parametrize("splits", [0, 1, 2, 3, 12, 16, 32])
-@pytest.mark.parametrize("H", [16, 32, 64, 128])
+@pytest.mark.parametrize("H", [16, 32, 48, 64, 80, 96, 112, 128])
 def test_sparse_mla_parity(dsa, H, splits):
     wl, batch, t, idx = mla_inputs(dsa, [3000, 700, 130, 2049], [1, 2, 1, 1], H, seed=H + splits)
     out, lse = run_mla(dsa, wl, batch, t, idx, splits)
