@@ -91,6 +91,7 @@ typedef enum {
 #define DSA_MAX_SEQS 4096
 #define DSA_KV8_PAGE_BYTES 41984      /* fp8 latent page: 64 x 640 B rows + 64 x 16 B scale records */
 #define DSA_MAX_WRITE_ITEMS (1 << 24) /* rows / tokens per quantiser or cache-writer call */
+#define DSA_NOALLOC_SCRATCH_BYTES (32u << 20) /* device scratch of dsa_sparse_mla_decode_noalloc */
 
 /* One step's batch description, shared by all four calls. */
 typedef struct {
@@ -198,6 +199,29 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
                           const uint16_t* kv_cache, int64_t kv_page_stride, const int32_t* indices,
                           int32_t k, float softmax_scale, int32_t num_splits, uint16_t* out,
                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_mla_decode_noalloc -- dsa_sparse_mla_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments, kernels and
+ * results without the workspace.  The split partials live in a device array
+ * inside the library, DSA_NOALLOC_SCRATCH_BYTES (32 MiB) on every device the
+ * call runs on, held until the process ends.  The call allocates nothing; on
+ * its first call on a device it looks that array's address up (with the
+ * device current).
+ *  num_splits  0 = the automatic split count, lowered until the partials
+ *              (splits * R * H * 2056 bytes) fit the array; n = forced, and a
+ *              forced count whose partials do not fit returns
+ *              DSA_ERR_UNSUPPORTED (nothing is launched).
+ *  Calls on one device share the array: two calls that overlap in time on one
+ *  device (different streams, or different threads) race and give undefined
+ *  results; calls ordered on one stream are safe.  Nothing in the array needs
+ *  clearing (a call writes every partial it reads).
+ */
+int dsa_sparse_mla_decode_noalloc(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads,
+                                  const uint16_t* kv_cache, int64_t kv_page_stride, const int32_t* indices,
+                                  int32_t k, float softmax_scale, int32_t num_splits, uint16_t* out, float* lse,
+                                  void* stream);
 
 /*
  * dsa_sparse_mla_decode_fp8 -- dsa_sparse_mla_decode over an fp8 latent cache,

@@ -8,5 +8,5 @@ from .binding import (  # noqa: F401
     DSAError, load, library_path, indexer_logits_paged, indexer_logits_prefill, topk,
     sparse_mla_decode, topk_workspace_bytes, sparse_mla_workspace_bytes, sparse_mla_pick_splits,
     indexer_q_quant_fp8, indexer_k_quant_and_cache, latent_cache_write, sparse_mla_decode_fp8,
-    latent_cache_write_fp8, Batch,
+    latent_cache_write_fp8, sparse_mla_decode_noalloc, Batch,
 )

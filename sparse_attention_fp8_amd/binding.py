@@ -65,6 +65,7 @@ def load():
         "dsa_topk": (ctypes.c_int, [B, vp, i64, i32, vp, vp, sz, vp]),
         "dsa_sparse_mla_decode": (ctypes.c_int, [B, vp, i32, vp, i64, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
         "dsa_sparse_mla_decode_fp8": (ctypes.c_int, [B, vp, i32, vp, i64, vp, i32, f32, i32, vp, vp, vp, sz, vp]),
+        "dsa_sparse_mla_decode_noalloc": (ctypes.c_int, [B, vp, i32, vp, i64, vp, i32, f32, i32, vp, vp, vp]),
         "dsa_latent_cache_write_fp8": (ctypes.c_int, [i32, vp, i64, vp, i64, vp, vp, i64, i32, vp]),
         "dsa_indexer_q_quant_fp8": (ctypes.c_int, [i32, vp, vp, vp, vp, vp]),
         "dsa_indexer_k_quant_and_cache": (ctypes.c_int, [i32, vp, i64, vp, vp, i64, i32, vp]),
@@ -249,6 +250,30 @@ def sparse_mla_decode(batch: Batch, q, kv_cache, indices, softmax_scale, out, ls
                                    int(kv_cache.shape[1]), _ptr(indices), k, float(softmax_scale),
                                    int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), wbytes, _stream(dev))
     _check(st, "dsa_sparse_mla_decode")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # the library's device array behind sparse_mla_decode_noalloc
+
+
+def sparse_mla_decode_noalloc(batch: Batch, q, kv_cache, indices, softmax_scale, out, lse, num_splits=0):
+    """dsa_sparse_mla_decode_noalloc: dsa_sparse_mla_decode with the split
+    partials in the library's own device array (nothing is allocated, here or
+    in the library).  Calls that overlap in time on one device race."""
+    lib = load()
+    dev = batch.device
+    R = batch.num_rows
+    _need(q, "q", torch.bfloat16, (R, None, KV_DIM), dev)
+    H = int(q.shape[1])
+    _need(kv_cache, "kv_cache", torch.bfloat16, (batch.num_pages, None), dev)
+    _need(indices, "indices", torch.int32, (R, None), dev)
+    k = int(indices.shape[1])
+    _need(out, "out", torch.bfloat16, (R, H, V_DIM), dev)
+    _need(lse, "lse", torch.float32, (R, H), dev)
+    st = lib.dsa_sparse_mla_decode_noalloc(ctypes.byref(batch.c_struct()), _ptr(q), H, _ptr(kv_cache),
+                                           int(kv_cache.shape[1]), _ptr(indices), k, float(softmax_scale),
+                                           int(num_splits), _ptr(out), _ptr(lse), _stream(dev))
+    _check(st, "dsa_sparse_mla_decode_noalloc")
     return out, lse
 
 

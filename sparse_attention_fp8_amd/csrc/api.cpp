@@ -191,10 +191,12 @@ size_t dsa_sparse_mla_workspace_bytes(const dsa_batch_t* batch, int32_t num_head
   return dsa::sparse_mla_workspace_bytes(batch->num_rows, num_heads, p);
 }
 
-int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads, const uint16_t* kv_cache,
-                          int64_t kv_page_stride, const int32_t* indices, int32_t k, float softmax_scale,
-                          int32_t num_splits, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+// Argument checks shared by dsa_sparse_mla_decode and its no-allocation
+// variant.  DSA_OK with *empty set means there is nothing to launch.
+static int check_sparse_mla(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads, const uint16_t* kv_cache,
+                            int64_t kv_page_stride, const int32_t* indices, int32_t k, float softmax_scale,
+                            int32_t num_splits, uint16_t* out, float* lse, bool* empty) {
+  *empty = true;
   int st = check_batch(batch);
   if (st != DSA_OK) return st;
   if (!heads_supported(num_heads))
@@ -213,6 +215,18 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
     if (!kv_cache) return fail(DSA_ERR_NULL, "kv_cache is NULL");
     if (!aligned(kv_cache, 16)) return fail(DSA_ERR_INVALID, "kv_cache must be 16-byte aligned");
   }
+  *empty = false;
+  return DSA_OK;
+}
+
+int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads, const uint16_t* kv_cache,
+                          int64_t kv_page_stride, const int32_t* indices, int32_t k, float softmax_scale,
+                          int32_t num_splits, uint16_t* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  bool empty = true;
+  const int st = check_sparse_mla(batch, q, num_heads, kv_cache, kv_page_stride, indices, k, softmax_scale,
+                                  num_splits, out, lse, &empty);
+  if (st != DSA_OK || empty) return st;
   const dsa::MlaPlan p = dsa::plan_sparse_mla(batch->num_rows, batch->max_seq_len, num_heads, k, num_splits, kTargetCUs);
   const size_t need = dsa::sparse_mla_workspace_bytes(batch->num_rows, num_heads, p);
   if (need > 0) {
@@ -224,6 +238,39 @@ int dsa_sparse_mla_decode(const dsa_batch_t* batch, const uint16_t* q, int32_t n
   return hip_status(dsa::launch_sparse_mla(to_args(batch), q, num_heads, kv_cache, kv_page_stride, indices, k,
                                            softmax_scale, p, out, lse, workspace, (hipStream_t)stream),
                     "dsa_sparse_mla_decode launch");
+}
+
+int dsa_sparse_mla_decode_noalloc(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads,
+                                  const uint16_t* kv_cache, int64_t kv_page_stride, const int32_t* indices,
+                                  int32_t k, float softmax_scale, int32_t num_splits, uint16_t* out, float* lse,
+                                  void* stream) {
+  bool empty = true;
+  const int st = check_sparse_mla(batch, q, num_heads, kv_cache, kv_page_stride, indices, k, softmax_scale,
+                                  num_splits, out, lse, &empty);
+  if (st != DSA_OK || empty) return st;
+  const size_t cap = dsa::static_scratch_bytes();
+  dsa::MlaPlan p = dsa::plan_sparse_mla(batch->num_rows, batch->max_seq_len, num_heads, k, num_splits, kTargetCUs);
+  size_t need = dsa::sparse_mla_workspace_bytes(batch->num_rows, num_heads, p);
+  if (need > cap && num_splits == 0) {
+    // the automatic count, lowered until the partials fit (one split needs none)
+    for (int s = p.splits - 1; s >= 1 && need > cap; --s) {
+      p = dsa::plan_sparse_mla(batch->num_rows, batch->max_seq_len, num_heads, k, s, kTargetCUs);
+      need = dsa::sparse_mla_workspace_bytes(batch->num_rows, num_heads, p);
+    }
+  }
+  if (need > cap)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_sparse_mla_decode_noalloc: %d splits need %zu scratch bytes, above its %zu-byte device array "
+                "(pass fewer splits, or use dsa_sparse_mla_decode with a workspace)",
+                p.splits, need, cap);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = dsa::static_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "dsa_sparse_mla_decode_noalloc scratch address");
+  }
+  return hip_status(dsa::launch_sparse_mla(to_args(batch), q, num_heads, kv_cache, kv_page_stride, indices, k,
+                                           softmax_scale, p, out, lse, scratch, (hipStream_t)stream),
+                    "dsa_sparse_mla_decode_noalloc launch");
 }
 
 int dsa_sparse_mla_decode_fp8(const dsa_batch_t* batch, const uint16_t* q, int32_t num_heads,

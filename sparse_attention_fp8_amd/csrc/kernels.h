@@ -37,6 +37,11 @@ hipError_t launch_sparse_mla(const BatchArgs& batch, const uint16_t* q, int H, c
                              const MlaPlan& plan, uint16_t* out, float* lse, void* workspace,
                              hipStream_t stream);
 
+// The device scratch behind dsa_sparse_mla_decode_noalloc: its size, and its
+// address on the current device (looked up on the first call per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_sparse_mla_fp8(const BatchArgs& batch, const uint16_t* q, int H, const uint8_t* kv8,
                                  int64_t kv8_stride, const int32_t* indices, int k, float softmax_scale,
                                  const MlaPlan& plan, uint16_t* out, float* lse, void* workspace,

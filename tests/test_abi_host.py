@@ -163,6 +163,29 @@ def test_sparse_mla_argument_checks(lib):
     assert mla_call(lib, b, ws_bytes=need - 1) == ERR_WORKSPACE
 
 
+def test_sparse_mla_noalloc_argument_checks(lib):
+    """The no-allocation variant takes the same checks; a forced split count
+    whose partials exceed its 32 MiB device array is rejected before any
+    device call (so this runs without a GPU)."""
+    f = lib.dsa_sparse_mla_decode_noalloc
+
+    def call(b, H=16, splits=0, **kw):
+        a = dict(q=FAKE, kv=FAKE, kv_stride=64 * 576, indices=FAKE, scale=0.07, out=FAKE, lse=FAKE)
+        a.update(kw)
+        return f(None if b is None else ctypes.byref(b), a["q"], H, a["kv"], a["kv_stride"], a["indices"], 2048,
+                 a["scale"], splits, a["out"], a["lse"], None)
+    assert call(None) == ERR_NULL
+    assert call(batch(), H=24) == ERR_UNSUPPORTED
+    assert call(batch(), kv_stride=64 * 576 + 4) == ERR_INVALID
+    assert call(batch(), lse=None) == ERR_NULL
+    assert call(batch(num_rows=0)) == OK
+    # 32 splits x 4096 rows x 128 heads of partials: far above 32 MiB
+    big = batch(num_rows=4096, max_seq_len=65536, bt_stride=1024)
+    assert call(big, H=128, splits=32) == ERR_UNSUPPORTED
+    msg = lib.dsa_last_error_message()
+    assert b"scratch" in msg and b"33554432" in msg
+
+
 def test_split_heuristic_and_workspace(lib):
     def splits(R, L, H):
         return lib.dsa_sparse_mla_pick_splits(ctypes.byref(batch(num_rows=R, max_seq_len=L, bt_stride=(L + 63) // 64)), H, 2048)
