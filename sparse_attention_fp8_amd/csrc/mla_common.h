@@ -39,6 +39,16 @@ __device__ __forceinline__ v4s lds_read_tr16(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(const __attribute__((address_space(3))) void*)p);
 }
 
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+// The packed pair is read back whole: element-wise reads of a bf16 vector
+// have given wrong lanes with this compiler.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const v2bf16 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   v8bf r;
   __builtin_memcpy(&r, &x, 16);

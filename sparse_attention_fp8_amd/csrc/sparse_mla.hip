@@ -64,6 +64,7 @@ constexpr int kChunks = kKvDim * 2 / 16;       // 72 sixteen-byte chunks per lat
 constexpr int kChunkGroups = kChunks / 8;      // 9 groups of 128 B per row
 constexpr int kRowGroups = kTile / 8;          // 8 groups of 8 rows per tile
 constexpr int kTileBytes = kTile * kChunks * 16;   // 73728
+constexpr float kRescaleLog2 = 8.f;                // probabilities stay below 2^8 (lazy rescaling)
 
 __device__ __attribute__((aligned(16))) uint4 g_zero_row[kChunks] = {};
 
@@ -101,7 +102,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   constexpr int RGW = kRowGroups / NW; // row groups each wave gathers
   constexpr int ND = RGW * kChunkGroups;   // gather loads per wave and tile
   static_assert(RGW * NW == kRowGroups, "waves must split the row groups evenly");
-  static_assert(DW % 128 == 0, "PV swizzle terms assume 128-dim aligned parts");
+  static_assert(DW % 64 == 0, "PV parts are whole 64-dim column groups");
   static_assert(ND + 2 < 64, "vmcnt range");
   static_assert(HGP * PVH == HT && TPV * HGP == NW, "PV roles must cover heads and dims");
   static_assert(TP > 1, "the tile maxima and sums are exchanged through LDS");
@@ -235,7 +236,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
     for (int i = 0; i < NDT; ++i) acc[hh][i] = v4f{0.f, 0.f, 0.f, 0.f};
     m_pv[hh] = kMaskSentinel;
   }
-  float m_run = kMaskSentinel;   // running max of the log2-domain scores of head h
+  float m_run = kMaskSentinel;   // reference max of the log2-domain scores of head h (see below)
   float l_part = 0.f;            // this lane's share of the running sum
 
   // DEEP pipeline: the copy of tile t + 2 goes out as soon as every wave is
@@ -325,24 +326,38 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
       __syncthreads();
 #pragma unroll
       for (int pp = 0; pp < TP; ++pp) tmax = fmaxf(tmax, sh.tmax[ht][pp][n16]);
-      const float m_new = fmaxf(m_run, tmax);
-      // v_exp_f32 directly: exp2f's extra scaling only matters for results
-      // below 2^-126, which are nothing next to the running maximum's 1.
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      // Lazy rescaling: a head's reference max moves only when the tile max
+      // passes it by more than kRescaleLog2 (or on its first tile with a valid
+      // key, when there is nothing to rescale).  The probabilities exp2(z - m)
+      // then stay below 2^kRescaleLog2 -- in range for bf16 and fp32 -- and the
+      // accumulators are rescaled only on those rare tiles (for these scores,
+      // about never after the first), not with a VALU pass on every tile;
+      // out = acc / l and lse = m + log2 l do not depend on which m was used.
+      // The scoring wave and every PV wave holding a head take the same
+      // decision from the same maxima.  v_exp_f32 directly: exp2f's extra
+      // scaling only matters below 2^-126.
+      auto advance = [](float& m, float tm, float& alpha) -> bool {
+        const bool first = m == kMaskSentinel;
+        const bool move = first || tm > m + kRescaleLog2;
+        alpha = (move && !first) ? __builtin_amdgcn_exp2f(m - tm) : 1.f;
+        m = move ? tm : m;
+        return move && !first;
+      };
+      float alpha;
+      bool rescale = advance(m_run, tmax, alpha);
+      const float m_new = m_run;
       float alpha_pv[PVH];
       if constexpr (PVH == 1) {
         alpha_pv[0] = alpha;
         m_pv[0] = m_new;
       } else {
+        rescale = false;
 #pragma unroll
         for (int hh = 0; hh < PVH; ++hh) {
           float tm = kMaskSentinel;
 #pragma unroll
           for (int pp = 0; pp < TP; ++pp) tm = fmaxf(tm, sh.tmax[hgp * PVH + hh][pp][n16]);
-          const float mn = fmaxf(m_pv[hh], tm);
-          alpha_pv[hh] = __builtin_amdgcn_exp2f(m_pv[hh] - mn);
-          m_pv[hh] = mn;
+          rescale |= advance(m_pv[hh], tm, alpha_pv[hh]);
         }
       }
       float psum = 0.f;
@@ -363,10 +378,12 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
         sh.p[ht][part * TPT + u][g][n16] = pk;
       }
       l_part = l_part * alpha + psum;
+      if (__ballot(rescale) != 0ull) {                 // rare: a head's maximum moved up
 #pragma unroll
-      for (int hh = 0; hh < PVH; ++hh)
+        for (int hh = 0; hh < PVH; ++hh)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[hh][dt] *= alpha_pv[hh];
+          for (int dt = 0; dt < NDT; ++dt) acc[hh][dt] *= alpha_pv[hh];
+      }
       __syncthreads();                                 // probabilities of all token tiles
 
       // O^T += V^T . P^T over the 64 tokens, 32 per MFMA: k slot i of lane group
@@ -395,6 +412,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
           for (int hh = 0; hh < PVH; ++hh)
             acc[hh][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[hh], acc[hh][dt], 0, 0, 0);
         }
+        asm volatile("" ::: "memory");   // the second step's reads stay behind the first's MFMAs (no spill at 64 heads)
       }
     }
 

@@ -47,7 +47,6 @@ constexpr int kPStride = kTile8 + 8;                 // bf16 per (group, head) r
 __device__ __attribute__((aligned(16))) uint4 g_zero_row8[kRow8 / 16] = {};
 
 typedef int v2i __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 
 // ds_read_b64_tr_b8: within each group of 16 lanes, lane n receives byte n % 8
 // of the 8-byte vectors addressed by lanes n / 8 + 2 j, j = 0..7 (checked by
@@ -70,14 +69,6 @@ __device__ __forceinline__ v8bf fp8x8_to_v8bf(uint32_t w0, uint32_t w1) {
   const uint4 u = make_uint4(fp8x2_to_bf16x2(w0, false), fp8x2_to_bf16x2(w0, true),
                              fp8x2_to_bf16x2(w1, false), fp8x2_to_bf16x2(w1, true));
   return as_v8bf(u);
-}
-
-// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
-// The packed pair is read back whole: element-wise reads of a bf16 vector
-// have given wrong lanes with this compiler.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const v2bf16 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
 }
 
 constexpr int kMaxTiles8 = DSA_MAX_TOPK / kTile8;   // 32 tiles per split at most
