@@ -159,11 +159,12 @@ int dsa_indexer_logits_prefill(const dsa_batch_t* batch, const uint8_t* q_fp8, c
  *  logits     [R, logits_stride] fp32, 16-byte aligned, logits_stride % 4 == 0
  *  k          1 <= k <= DSA_MAX_TOPK; rows may hold up to (65536 / k) * 131072
  *             keys (4,194,304 for k = 2048), longer max_seq_len is UNSUPPORTED.
- *             Rows longer than 32768 keys are cut into 32768-key chunks whose
- *             top k are candidates; beyond 4 chunks, groups of 4 chunks are
- *             first reduced to their top k (exact: a winner of the row is a
- *             winner of its chunk and of its group -- the pages' chunking
- *             argument, review thread).
+ *             With max_seq_len <= 65536 every row is selected by one
+ *             workgroup.  Longer rows are cut into 32768-key chunks whose top k
+ *             are candidates; beyond 4 chunks, groups of 4 chunks are first
+ *             reduced to their top k (exact: a winner of the row is a winner
+ *             of its chunk and of its group -- the pages' chunking argument,
+ *             review thread).
  *  indices    [R, k] int32
  *  workspace  device scratch of at least dsa_topk_workspace_bytes(batch, k)
  *             bytes (may be NULL when that is 0); 256-byte aligned.

@@ -53,6 +53,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kChunk = 32768;          // keys per workgroup in the row pass
+constexpr int kSingleMax = 2 * kChunk; // longest row one workgroup selects from (two segments)
 constexpr int kMergeMax = 65536;       // candidates per row in the merge pass
 constexpr int kGroupChunks = 4;        // chunks one group merge reduces to k candidates
 constexpr int kBins = 2048;
@@ -401,7 +402,8 @@ __device__ Selection radix_select(const Keys<KPT>& keys, int k, Shared& sh) {
 // emitted: slots [0, that) each exactly once -- k, unless the row holds fewer
 // than k orderable keys (some NaNs are not orderable, see load_keys).
 template <int KPT, class Emit>
-__device__ int emit_selected(const Keys<KPT>& keys, Selection sel, int k, Shared& sh, Emit emit) {
+__device__ int emit_selected(const Keys<KPT>& keys, Selection sel, int k, Shared& sh, Emit emit,
+                             int* eq_total = nullptr) {
   MaskT<KPT> gtb = 0, eqb = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) gtb |= (MaskT<KPT>)(keys.v[j] > sel.threshold) << j;
@@ -436,6 +438,7 @@ __device__ int emit_selected(const Keys<KPT>& keys, Selection sel, int k, Shared
     ++pos;
     selb &= selb - 1;
   }
+  if (eq_total) *eq_total = tot >> 12;               // keys equal to the threshold, taken or not
   return min(k, (tot & 0xFFF) + min(tot >> 12, sel.need_eq));
 }
 
@@ -504,6 +507,54 @@ __global__ void __launch_bounds__(kThreads) topk_rows_kernel(TopkArgs a) {
     ck[i] = pos >= 0 ? float_key(row[lo + pos]) : 0u;   // key 0: never selected again
   }
   if (threadIdx.x == 0) a.cand_count[slot] = k;
+}
+
+// Rows of up to kSingleMax = 2 kChunk keys, one workgroup each, no
+// candidates and no merge launch: thread t holds keys [32 t, 32 t + 32) of
+// the row (segment 0) and [kChunk + 32 t, kChunk + 32 t + 32) (segment 1) in
+// registers, each segment staged through the same LDS area in turn.  The
+// radix select counts the 64 keys of every thread whatever their positions;
+// the emission then walks segment 0 and segment 1 in turn, so the output
+// stays in ascending index order and ties at the threshold go to segment 0's
+// (lower) indices first.  Rows of at most kChunk keys take the 32-key path.
+__global__ void __launch_bounds__(kThreads) topk_rows64_kernel(TopkArgs a) {
+  __shared__ TopkLds<32> lds;
+  Shared& sh = lds.s;
+  const int r = blockIdx.x;
+  int b, e;
+  seq_and_extent_wave(a.batch, r, b, e);
+  const int k = a.k;
+  const float* row = a.logits + (int64_t)r * a.logits_stride;
+  int32_t* out = a.indices + (int64_t)r * k;
+  if (e <= k) {
+    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < e ? i : -1;
+    return;
+  }
+  Keys<32> k0;
+  load_keys(k0, row, min(e, kChunk), lds.stage);
+  __syncthreads();   // every wave has read its keys: the staging area is free
+  if (e <= kChunk) {
+    const Selection sel = radix_select(k0, k, sh);
+    const int emitted = emit_selected(k0, sel, k, sh, [&](int pos, int i) { out[pos] = i; });
+    for (int i = emitted + (int)threadIdx.x; i < k; i += kThreads) out[i] = -1;
+    return;
+  }
+  Keys<32> k1;
+  load_keys(k1, row + kChunk, e - kChunk, lds.stage);   // 128 KB in: kChunk * 4 bytes is 16-byte aligned
+  __syncthreads();   // segment 1 read back; the selection state (zeroed by both loads) is visible
+  Keys<64> kk;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    kk.v[j] = k0.v[j];
+    kk.v[32 + j] = k1.v[j];
+  }
+  const Selection sel = radix_select(kk, k, sh);
+  int eq0 = 0;
+  const int n0 = emit_selected(k0, sel, k, sh, [&](int pos, int i) { out[pos] = i; }, &eq0);
+  __syncthreads();   // the second emission's scan reuses sh.wave_tot
+  const Selection sel1{sel.threshold, max(0, sel.need_eq - eq0)};
+  const int n1 = emit_selected(k1, sel1, k - n0, sh, [&](int pos, int i) { out[n0 + pos] = kChunk + i; });
+  for (int i = n0 + n1 + (int)threadIdx.x; i < k; i += kThreads) out[i] = -1;
 }
 
 // First level of the merge for rows of more than kGroupChunks chunks: group g
@@ -603,7 +654,11 @@ __global__ void __launch_bounds__(kThreads) topk_merge_kernel(TopkArgs a) {
 
 }  // namespace
 
-int topk_num_chunks(int max_seq_len) { return max_seq_len <= kChunk ? 1 : (max_seq_len + kChunk - 1) / kChunk; }
+// Rows of up to kSingleMax keys are selected by one workgroup; longer rows in
+// kChunk-key chunks and a candidate merge.
+int topk_num_chunks(int max_seq_len) {
+  return max_seq_len <= kSingleMax ? 1 : (max_seq_len + kChunk - 1) / kChunk;
+}
 
 // Rows of up to kGroupChunks chunks merge in one level (candidates <=
 // kGroupChunks * k), longer rows in two (final candidates <= groups * k).
@@ -660,10 +715,13 @@ hipError_t launch_topk(const BatchArgs& batch, const float* logits, int64_t logi
       a.grp_count = reinterpret_cast<int32_t*>(ws + off);
     }
   }
-  // keys per thread: the smallest of 8 / 16 / 32 that covers a chunk
+  // keys per thread: the smallest of 8 / 16 / 32 that covers a chunk, or two
+  // 32-key segments for single rows of up to kSingleMax keys
   const int longest = a.nchunks > 1 ? kChunk : batch.max_seq_len;
   const int64_t grid = (int64_t)batch.num_rows * a.nchunks;
-  if (longest <= 8 * kThreads) {
+  if (a.nchunks == 1 && longest > kChunk) {
+    hipLaunchKernelGGL(topk_rows64_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  } else if (longest <= 8 * kThreads) {
     hipLaunchKernelGGL(topk_rows_kernel<8>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   } else if (longest <= 16 * kThreads) {
     hipLaunchKernelGGL(topk_rows_kernel<16>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);

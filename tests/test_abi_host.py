@@ -109,11 +109,12 @@ def test_topk_argument_checks(lib):
 
 
 def test_topk_workspace_sizes(lib):
-    # rows that fit one 32768-key chunk need no workspace
+    # rows of up to 65536 keys are selected by one workgroup: no workspace
     assert lib.dsa_topk_workspace_bytes(ctypes.byref(batch(max_seq_len=32768, bt_stride=512)), 2048) == 0
-    b = batch(max_seq_len=65536, bt_stride=1024, num_rows=4096)
+    assert lib.dsa_topk_workspace_bytes(ctypes.byref(batch(max_seq_len=65536, bt_stride=1024)), 2048) == 0
+    b = batch(max_seq_len=65537, bt_stride=1025, num_rows=4096)
     need = lib.dsa_topk_workspace_bytes(ctypes.byref(b), 2048)
-    assert need >= 4096 * 2 * 2048 * 8 and need % 256 == 0      # two 32768-key chunks per row
+    assert need >= 4096 * 3 * 2048 * 8 and need % 256 == 0      # longer: three 32768-key chunks per row
     assert lib.dsa_topk_workspace_bytes(None, 2048) == 0
     # past four chunks the merge adds a level: groups of four chunks keep k each
     one_m = batch(max_seq_len=1 << 20, bt_stride=1 << 14, num_rows=2)
