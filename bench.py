@@ -6,10 +6,10 @@ rows (split-KV partials + merge when the split heuristic picks more than one).
 Inputs are seeded synthetic tensors resident in HBM before timing starts; the
 timed steps rotate through several copies of the caches so that the 256 MB
 Infinity Cache cannot serve one step's reads from the previous step.  The
-timed region replays a HIP graph holding one step per cache copy back to back
-(as a decoder replays its layers' steps inside one graph, so a graph launch is
-paid once per `copies` steps); the one-graph-per-step rate is reported beside
-it.
+timed region replays a HIP graph holding ten steps back to back, rotating
+through the copies (as a decoder replays its layers' steps inside one graph,
+so a graph launch is paid once per many steps); the one-graph-per-step rate is
+reported beside it.
 
 Prints one JSON line: metric, value = steps/s of the headline workload (by
 default c5, MTP decode over 64 sequences at 128 MLA heads: the largest decode
@@ -35,6 +35,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0
+CHAIN_STEPS = 10               # steps per timed graph (at least one per cache copy)
+WARM_S = 0.3                   # untimed warm-up (whole steps) before the timed region, seconds
 
 
 def parse():
@@ -311,8 +313,11 @@ def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True
     torch.cuda.synchronize()
 
     # One HIP graph per cache copy holds one whole step, and a chain graph holds
-    # one step per copy back to back.  The timed region runs exactly `steps`
-    # steps: steps // copies chain replays, then single-step graphs.
+    # `chain_len` steps back to back, rotating through the copies (a decoder
+    # replays its layers' DSA steps inside one graph the same way, so a graph
+    # launch is paid once per many steps).  The timed region runs exactly
+    # `steps` steps: steps // chain_len chain replays, then single-step graphs.
+    chain_len = max(copies, min(args.steps, CHAIN_STEPS))
     step_graphs = []
     for c in range(copies):
         g = torch.cuda.CUDAGraph()
@@ -321,8 +326,8 @@ def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True
         step_graphs.append(g)
     chain = torch.cuda.CUDAGraph()
     with torch.cuda.graph(chain):
-        for c in range(copies):
-            step(c)
+        for c in range(chain_len):
+            step(c % copies)
     # Per-stage graphs: `reps` launches of one entry point, rotating copies, so
     # the stage's average launch duration is measured on its own stream.
     reps = 2 * copies
@@ -336,16 +341,27 @@ def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True
     torch.cuda.synchronize()
     for i in range(args.warmup):
         step_graphs[i % copies].replay()
-    chain.replay()
+    # Untimed warm-up until the clocks have settled: whole steps (chain
+    # replays) for at least WARM_S seconds of GPU time.  A c5 step measured
+    # after 5 warm-up steps only reads ~15 % slower than in steady state.
+    t_warm = time.perf_counter()
+    warm_replays = 0
+    while True:
+        chain.replay()
+        warm_replays += 1
+        if warm_replays % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_warm >= WARM_S:
+                break
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(args.steps // copies):
+    for _ in range(args.steps // chain_len):
         chain.replay()
-    for i in range(args.steps % copies):
-        step_graphs[i].replay()
+    for i in range(args.steps % chain_len):
+        step_graphs[i % copies].replay()
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -392,9 +408,10 @@ def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True
         "config": {"workload": synth.CONFIGS[name], "name": name, "rows": R, "mla_heads": H,
                    "topk": k, "splits": nsplits, "cache_copies": copies,
                    "seed": seed if seed is not None else synth.DEFAULT_SEEDS[name]},
-        "timing": f"HIP graph replays: a graph of {copies} steps (one per cache copy) replayed "
-                  f"{args.steps // copies} times plus {args.steps % copies} single-step graphs; stage times from "
-                  f"graphs of {reps} launches of one entry point",
+        "timing": f"HIP graph replays after {args.warmup} warm-up steps and {warm_replays * chain_len} more "
+                  f"untimed steps ({WARM_S} s, clocks settled): a graph of {chain_len} steps (rotating {copies} "
+                  f"cache copies) replayed {args.steps // chain_len} times plus {args.steps % chain_len} single-step "
+                  f"graphs; stage times from graphs of {reps} launches of one entry point",
         "rows": R,
     }
     if details:
