@@ -49,6 +49,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Lazy rescaling of the online softmax: a head's reference max m (log2
+// domain) moves only when a tile's max tm passes it by more than
+// kRescaleLog2, or on its first tile with a valid key (m still the -1e30
+// sentinel, nothing accumulated yet).  The probabilities exp2(z - m) then stay
+// below 2^kRescaleLog2, in range for bf16 and fp32, and out = acc / l and
+// lse = m + log2 l do not depend on which m was used, so the accumulators need
+// rescaling (by alpha) only on the tiles where this returns true.
+constexpr float kRescaleLog2 = 8.f;
+__device__ __forceinline__ bool lazy_max_advance(float& m, float tm, float& alpha) {
+  const bool first = m == kMaskSentinel;
+  const bool move = first || tm > m + kRescaleLog2;
+  alpha = (move && !first) ? __builtin_amdgcn_exp2f(m - tm) : 1.f;   // v_exp_f32 directly
+  m = move ? tm : m;
+  return move && !first;
+}
+
 __device__ __forceinline__ v8bf as_v8bf(uint4 x) {
   v8bf r;
   __builtin_memcpy(&r, &x, 16);

@@ -64,7 +64,6 @@ constexpr int kChunks = kKvDim * 2 / 16;       // 72 sixteen-byte chunks per lat
 constexpr int kChunkGroups = kChunks / 8;      // 9 groups of 128 B per row
 constexpr int kRowGroups = kTile / 8;          // 8 groups of 8 rows per tile
 constexpr int kTileBytes = kTile * kChunks * 16;   // 73728
-constexpr float kRescaleLog2 = 8.f;                // probabilities stay below 2^8 (lazy rescaling)
 
 __device__ __attribute__((aligned(16))) uint4 g_zero_row[kChunks] = {};
 
@@ -336,15 +335,8 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
       // The scoring wave and every PV wave holding a head take the same
       // decision from the same maxima.  v_exp_f32 directly: exp2f's extra
       // scaling only matters below 2^-126.
-      auto advance = [](float& m, float tm, float& alpha) -> bool {
-        const bool first = m == kMaskSentinel;
-        const bool move = first || tm > m + kRescaleLog2;
-        alpha = (move && !first) ? __builtin_amdgcn_exp2f(m - tm) : 1.f;
-        m = move ? tm : m;
-        return move && !first;
-      };
       float alpha;
-      bool rescale = advance(m_run, tmax, alpha);
+      bool rescale = lazy_max_advance(m_run, tmax, alpha);
       const float m_new = m_run;
       float alpha_pv[PVH];
       if constexpr (PVH == 1) {
@@ -357,7 +349,7 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
           float tm = kMaskSentinel;
 #pragma unroll
           for (int pp = 0; pp < TP; ++pp) tm = fmaxf(tm, sh.tmax[hgp * PVH + hh][pp][n16]);
-          rescale |= advance(m_pv[hh], tm, alpha_pv[hh]);
+          rescale |= lazy_max_advance(m_pv[hh], tm, alpha_pv[hh]);
         }
       }
       float psum = 0.f;

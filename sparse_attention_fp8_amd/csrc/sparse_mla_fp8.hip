@@ -345,11 +345,12 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
 #pragma unroll
         for (int pp = 0; pp < TP; ++pp) tmax = fmaxf(tmax, sh.tmax[ht][pp][n16]);
       }
-      const float m_new = fmaxf(m_run, tmax);
-      // v_exp_f32 directly: exp2f's extra scaling only matters for results
-      // below 2^-126, which are nothing next to the running maximum's 1.
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      // Lazy rescaling, as the bf16 kernel: the reference max moves only when
+      // the tile max passes it by more than kRescaleLog2 (or on the first
+      // tile with a valid key), so the accumulators are rescaled only then.
+      float alpha;
+      const bool rescale = lazy_max_advance(m_run, tmax, alpha);
+      const float m_new = m_run;
       float psum = 0.f;
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
@@ -377,8 +378,10 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
         }
       }
       l_part = l_part * alpha + psum;
+      if (__ballot(rescale) != 0ull) {                 // rare: a head's maximum moved up
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      }
       __syncthreads();                                 // P' of all token tiles
 
       // O^T += V^T . P'^T over the 64 tokens, 32 per MFMA: k slot j of lane
