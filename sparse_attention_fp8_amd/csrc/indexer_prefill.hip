@@ -25,8 +25,12 @@
 //    s + 1 is in flight while stage s is multiplied.
 //  * Workgroup ids run over the key chunks fastest, so the 8 XCDs each serve
 //    two key chunks from their own L2 to every row block.
-//  * Keys s >= e_r are masked (written -inf when clean_logits); chunks cover
-//    the whole logits stride, so no separate tail pass is needed.
+//  * Per-row causal bound with an early exit: only the stages holding a key
+//    some row of the block can see are copied and multiplied; inside them
+//    keys s >= e_r are masked.  With clean_logits the rest of the chunk (to
+//    the logits stride) only gets -inf stores, so a block whose rows see a
+//    short prefix pays for its causal extent, not the whole rectangle.
+//    Chunks cover the whole logits stride, so no separate tail pass is needed.
 #include "common.h"
 #include "kernels.h"
 
@@ -43,7 +47,9 @@ constexpr int kStageKeys = 256;                  // keys per LDS stage (four pag
 constexpr int kPagesPerChunk = kChunkKeys / kPage;
 constexpr int kStageCodeBytes = kStageKeys * kIdxDim;    // 32 KB
 constexpr int kDmaPerWave = kStageCodeBytes / 1024 / kWavesPf;   // 1 KB copies per wave and stage
-constexpr int kScaleWaves = kStageKeys / kPage;          // waves that also copy one page's scales
+constexpr int kPagesPerStage = kStageKeys / kPage;       // also the waves that copy one page's scales
+static_assert(kDmaPerWave * 8 <= kPage && kPage % (kDmaPerWave * 8) == 0, "a wave's copy blocks lie in one page");
+static_assert(kPagesPerStage <= kWavesPf, "one wave per page's scales");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -72,7 +78,6 @@ struct PrefillArgs {
 struct PrefillShared {
   unsigned char codes[2][kStageCodeBytes];   // swizzled key rows
   float scales[2][kStageKeys];
-  int page[kPagesPerChunk];                  // physical page of each page of the chunk (-1: none)
 };
 
 // One query row of a wave: q as MFMA A operands and the head weights of the
@@ -108,46 +113,61 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
   if (key0 >= key_end) return;
   // stages that hold a key some row of the block can see
   const int live = e_max > key0 ? (min(e_max, key_end) - key0 + kStageKeys - 1) / kStageKeys : 0;
-  const int nstages = a.clean ? (key_end - key0 + kStageKeys - 1) / kStageKeys : live;
+  // Clean logits: -inf over keys [max(e_r, key0), key_end) of every row of the
+  // block, stored here (the product stores of those keys are dropped by the
+  // row's buffer range below); aligned float4 stores, scalar at the ends.
+  if (a.clean) {
+    for (int ri = wave; ri < nrows; ri += kWavesPf) {
+      float* rowp = a.logits + (int64_t)(row0 + ri) * a.logits_stride;
+      const int c0 = max(extent(row0 + ri), key0);
+      const int c4 = min((c0 + 3) & ~3, key_end);
+      if (lane < c4 - c0) rowp[c0 + lane] = -INFINITY;
+      for (int c = c4 + 4 * lane; c < key_end; c += 256) {
+        if (c + 3 < key_end) *reinterpret_cast<float4*>(rowp + c) = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        else
+          for (int x = c; x < key_end; ++x) rowp[x] = -INFINITY;
+      }
+    }
+  }
+  const int nstages = live;
   if (nstages <= 0) return;
 
-  // physical pages of the chunk
+  // Physical pages of the chunk, lane p of every wave holding page p (-1:
+  // none); a copy picks its page with readlane (a scalar, no LDS round trip).
   const int pages_b = (L + kPage - 1) / kPage;
-  if (wave == 0) {
+  int pg = -1;
+  {
     const int j = kc * kPagesPerChunk + lane;
-    int id = -1;
     if (j < pages_b && lane < kPagesPerChunk) {
-      id = a.batch.block_table[(int64_t)b * a.batch.bt_stride + j];
-      if (id < 0 || id >= a.batch.num_pages) id = -1;
+      const int id = a.batch.block_table[(int64_t)b * a.batch.bt_stride + j];
+      pg = (id >= 0 && id < a.batch.num_pages) ? id : -1;
     }
-    if (lane < kPagesPerChunk) sh.page[lane] = id;
   }
-  __syncthreads();
+  const unsigned char* const zero_src = reinterpret_cast<const unsigned char*>(g_zero_kv);
 
   // Copy of stage st into buffer buf: wave w fills 1 KB blocks w * kDmaPerWave
-  // + i (8 key rows each); lane l fills slot l % 8 of row l / 8 of the block
-  // with chunk (l % 8) ^ swz(row), so every 8 lanes read one whole 128-byte
-  // key row.  The first kScaleWaves waves also copy one page's 256 scale bytes
-  // (lanes 0-15).
+  // + i (8 key rows each, all in page st * kPagesPerStage + w * kDmaPerWave /
+  // 8); lane l fills slot l % 8 of row l / 8 of the block with chunk (l % 8) ^
+  // swz(row), so every 8 lanes read one whole 128-byte key row.  The first
+  // kPagesPerStage waves also copy one page's 256 scale bytes (lanes 0-15).
   auto copy_stage = [&](int st, int buf) __attribute__((always_inline)) {
     const uint32_t dst = lds_addr(sh.codes[buf]);
+    const int id = __builtin_amdgcn_readlane(pg, st * kPagesPerStage + (wave * kDmaPerWave * 8) / kPage);
+    const unsigned char* base = id >= 0 ? a.cache + (int64_t)id * a.page_stride : zero_src;
+    // Key row n = 8 blk + l / 8 of the stage: swz(n) = (4 blk + l / 16) & 7 =
+    // l / 16 + 4 (blk & 1), so the slot offsets take two per-lane values.
+    const uint32_t slot = 16u * (uint32_t)((lane & 7) ^ (lane >> 4));
+    const uint32_t row = id >= 0 ? (uint32_t)(lane >> 3) * kIdxDim : 0u;
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
       const int blk = wave * kDmaPerWave + i;
-      const int n = 8 * blk + (lane >> 3);              // key row within the stage
-      const int key = st * kStageKeys + n;              // key within the chunk
-      const int id = sh.page[key >> 6];
-      const int c = (lane & 7) ^ swz(n);
-      const unsigned char* src = id >= 0
-          ? a.cache + (int64_t)id * a.page_stride + (key & 63) * kIdxDim + 16 * c
-          : reinterpret_cast<const unsigned char*>(g_zero_kv) + 16 * c;
-      lds_dma16(src, dst + blk * 1024);
+      const uint32_t off = (id >= 0 ? (uint32_t)(((8 * blk) & 63) * kIdxDim) : 0u) + row + (slot ^ ((blk & 1) ? 64u : 0u));
+      lds_dma16(base + off, dst + blk * 1024);
     }
-    if (wave < kScaleWaves && lane < 16) {
-      const int id = sh.page[kScaleWaves * st + wave];
-      const unsigned char* src = id >= 0 ? a.cache + (int64_t)id * a.page_stride + kIdxScaleOff + 16 * lane
-                                         : reinterpret_cast<const unsigned char*>(g_zero_kv) + 16 * lane;
-      lds_dma16(src, lds_addr(&sh.scales[buf][kPage * wave]));
+    if (wave < kPagesPerStage) {
+      const int ids = __builtin_amdgcn_readlane(pg, st * kPagesPerStage + wave);
+      const unsigned char* src = ids >= 0 ? a.cache + (int64_t)ids * a.page_stride + kIdxScaleOff : zero_src;
+      if (lane < 16) lds_dma16(src + 16 * lane, lds_addr(&sh.scales[buf][kPage * wave]));
     }
   };
 
@@ -193,70 +213,138 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
     boff[c] = nb * kIdxDim + 16 * (chunk ^ swz(nb));
   }
 
-  // Epilogue of one row and 32 keys: weighted ReLU head sum (in-lane over the
-  // lane's 32 heads, then lanes 0-31 add lanes 32-63 with a lane swap), K
-  // scale, masked store.
-  auto epilogue = [&](const RowOperands& o, const v16f* acc, int row, int er, bool hr, int key, float scale)
-      __attribute__((always_inline)) {
-    float p[4] = {0.f, 0.f, 0.f, 0.f};
+  // Logits stores of this wave's rows go through buffer resources based at
+  // the chunk start of the row with the row's causal part of the chunk,
+  // [key0, min(e_r, key_end)), as their range: stores of keys past e_r (and
+  // of lanes 32-63, which hold copies of lanes 0-31's sums) fall outside it
+  // and the hardware drops them, so the step body has no compares or
+  // branches and its MFMAs and VALU work can be interleaved freely.
+  constexpr uint32_t kDrop = 0x7FFF0000u;
+  __amdgpu_buffer_rsrc_t out_rsrc[kRowsPerWave];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int span = has_row[j] ? max(0, min(e_r[j], key_end) - key0) : 0;
+    out_rsrc[j] = __builtin_amdgcn_make_buffer_rsrc(a.logits + (int64_t)rr[j] * a.logits_stride + key0, (short)0,
+                                                    span * 4, 0x00020000);
+  }
+  const uint32_t lane_off = hb == 0 ? 4u * (uint32_t)nb : kDrop;
+
+  // Epilogue of row j and the 32 keys at chunk offset kb + nb: weighted ReLU
+  // head sum (in-lane over the lane's 32 heads in two chains, then lanes 0-31
+  // add lanes 32-63 with one lane swap of the chains' sum held twice) times
+  // the K scale.
+  auto epi_value = [&](int j, const v16f* acc, float scale) __attribute__((always_inline)) {
+    float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i & 3] = fmaf(o.wr[mt][i], relu_finite(acc[mt][i]), p[i & 3]);
-    float s = (p[0] + p[1]) + (p[2] + p[3]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    s += __uint_as_float(sw[1]);
-    const float v = s * scale;
-    if (hr && hb == 0 && key < key_end) {
-      float* dst = a.logits + (int64_t)row * a.logits_stride + key;
-      if (key < er) *dst = v;
-      else if (a.clean) *dst = -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i) p0 = fmaf(ro[j].wr[0][i], relu_finite(acc[0][i]), p0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p1 = fmaf(ro[j].wr[1][i], relu_finite(acc[1][i]), p1);
+    float x = p0 + p1, y = p0 + p1;
+    asm volatile("" : "+v"(y));      // two registers, so the swap needs no copies
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * scale;
+  };
+  auto epi_store = [&](int j, float v, int kb) __attribute__((always_inline)) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rsrc[j], lane_off + 4u * (uint32_t)kb, 0, 0);
+  };
+  auto epilogue = [&](int j, const v16f* acc, float scale, int kb) __attribute__((always_inline)) {
+    epi_store(j, epi_value(j, acc, scale), kb);
   };
 
-  auto compute_stage = [&](int st, int buf) __attribute__((always_inline)) {
-    constexpr int kSteps = kStageKeys / 32;
-#pragma unroll 2
-    for (int step = 0; step < kSteps; ++step) {
-      const unsigned char* tb = sh.codes[buf] + step * 32 * kIdxDim;
-      v8i bop[2];
+  // B operand (32 keys x 128 dims, this lane's slots) and K scale of one step.
+  v8i bop[2];
+  auto load_b = [&](int buf, int step, float& sc) __attribute__((always_inline)) {
+    const unsigned char* tb = sh.codes[buf] + step * 32 * kIdxDim;
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const v4i x0 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh]);
-        const v4i x1 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh + 1]);
-        bop[kh] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      }
-      const float scale = sh.scales[buf][step * 32 + nb];
-      v16f z;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) z[i] = 0.f;
-      v16f acc[kRowsPerWave][2];
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[mt][0], bop[0], z, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-          acc[j][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[mt][1], bop[1], acc[j][mt],
-                                                                       0, 0, 0, 0, 0, 0);
-      const int key = key0 + st * kStageKeys + step * 32 + nb;
-#pragma unroll
-      for (int j = 0; j < kRowsPerWave; ++j) epilogue(ro[j], acc[j], rr[j], e_r[j], has_row[j], key, scale);
+    for (int kh = 0; kh < 2; ++kh) {
+      const v4i x0 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh]);
+      const v4i x1 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh + 1]);
+      bop[kh] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     }
+    sc = sh.scales[buf][step * 32 + nb];
+  };
+  auto mfma_row = [&](int j, v16f* acc) __attribute__((always_inline)) {
+    v16f z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[0][0], bop[0], z, 0, 0, 0, 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[1][0], bop[0], z, 0, 0, 0, 0, 0, 0);
+    acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[0][1], bop[1], acc[0], 0, 0, 0, 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[1][1], bop[1], acc[1], 0, 0, 0, 0, 0, 0);
+  };
+  // Issue order of a half step: one MFMA per 19 VALU operations of the
+  // epilogue (76 in all); with `reload`, the next step's B operand is read
+  // into the same registers as soon as the MFMAs that use them have issued
+  // (K half 0 after the second MFMA, K half 1 and the scale after the fourth).
+  auto interleave = [&](bool reload) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
+    __builtin_amdgcn_sched_barrier(0);    // nothing moves across half steps
   };
 
-  // Double-buffered stages: the copy of stage st + 1 is in flight while stage
-  // st is multiplied; each wave waits for its own copies before the barrier.
+  // Software pipeline over steps of 32 keys, two rows per wave: the MFMAs of
+  // one row run while the VALU epilogue of the other row's previous product
+  // is issued (row 0 of step t + 1 beside row 1 of step t, row 1 of step t
+  // beside row 0 of step t).  Stages of 256 keys are double-buffered: the
+  // copy of stage st + 1 is in flight while stage st is multiplied; each wave
+  // waits for its own copies before the barrier that opens a stage.
+  v16f acc0[2], acc1[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc1[mt][i] = 0.f;
+  float sc = 0.f, sc_prev = 0.f;
+  int kb_prev = key_end - key0;        // the first stage has no previous step: its store is dropped
+  // The last two logits of a stage are stored after the next stage's barrier:
+  // the wait before that barrier (for this wave's copies) then does not also
+  // wait for stores issued just before it.
+  float held0 = 0.f, held1 = 0.f;
+  int kb_held = key_end - key0 + 32;  // nothing held before the first stage: both stores dropped
   copy_stage(0, 0);
   for (int st = 0; st < nstages; ++st) {
+    const int buf = st & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();            // stage st landed; buffer (st + 1) & 1 is free
-    if (st + 1 < nstages) copy_stage(st + 1, (st + 1) & 1);
-    compute_stage(st, st & 1);
+    if (st + 1 < nstages) copy_stage(st + 1, buf ^ 1);
+    load_b(buf, 0, sc);
+    mfma_row(0, acc0);
+    epilogue(1, acc1, sc_prev, kb_prev);
+    epi_store(1, held1, kb_held - 32);
+    epi_store(0, held0, kb_held);
+    interleave(false);
+#pragma unroll
+    for (int step = 0; step < kStageKeys / 32; ++step) {
+      const int kb = st * kStageKeys + step * 32;
+      const bool last = step + 1 == kStageKeys / 32;
+      const float sc_cur = sc;
+      mfma_row(1, acc1);
+      if (!last) epilogue(0, acc0, sc_cur, kb);
+      else held0 = epi_value(0, acc0, sc_cur);
+      if (!last) load_b(buf, step + 1, sc);
+      interleave(!last);
+      if (!last) {
+        mfma_row(0, acc0);
+        if (step + 2 < kStageKeys / 32) epilogue(1, acc1, sc_cur, kb);
+        else held1 = epi_value(1, acc1, sc_cur);
+        interleave(false);
+      } else {
+        sc_prev = sc_cur;
+        kb_prev = kb;
+        kb_held = kb;
+      }
+    }
   }
+  epi_store(1, held1, kb_held - 32);
+  epi_store(0, held0, kb_held);
+  epilogue(1, acc1, sc_prev, kb_prev);
 }
 
 }  // namespace

@@ -146,6 +146,25 @@ def test_indexer_dirty_leaves_tail(dsa, prefill):
 
 
 @pytest.mark.parametrize("prefill", [False, True], ids=["paged", "prefill"])
+def test_indexer_clean_short_prefix_wide_stride(dsa, prefill):
+    """clean_logits where most of each row lies past its causal extent: a
+    300-row prefill of a 300-token sequence (extents 1..300), 40 rows at the
+    end of 2100 tokens, 50 rows of a 20-token sequence (30 rows see nothing),
+    and a logits stride of three 4096-key chunks plus a ragged 132: whole
+    chunks, whole stages and stage tails past every extent must read -inf,
+    and every column must be written (the buffer starts as NaN)."""
+    wl = synth.make_workload([300, 2100, 20], [300, 40, 50], 16, seed=77, spare_pages=3, poison=True)
+    batch, t = to_dev(wl)
+    stride = 3 * 4096 + 132
+    got = run_indexer(dsa, wl, batch, t, stride, clean=True, prefill=prefill).cpu().numpy()
+    assert not np.isnan(got).any(), "unwritten logits columns"
+    ref, mag, ext = oracle_indexer(wl, stride, clean=True)
+    for r, e in enumerate(ext):
+        assert np.isneginf(got[r, e:]).all(), f"row {r}: columns past e_r={e} are not -inf"
+    check_logits(got, ref, mag, f"clean_wide/{'prefill' if prefill else 'paged'}")
+
+
+@pytest.mark.parametrize("prefill", [False, True], ids=["paged", "prefill"])
 def test_indexer_fp8_mfma_group_sum(dsa, prefill):
     """The arithmetic fact the logits tolerance rests on, pinned through the
     public API: one head (w = 1) whose dot has two non-zero products, a large
