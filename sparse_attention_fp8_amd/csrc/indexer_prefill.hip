@@ -5,32 +5,37 @@
 // K-side scale applied to the fp32 dot):
 //   logits[r, s] = sum_h w[r, h] * relu(q[r, h, :] . k[s, :]) * kscale[s],  s < e_r,
 // organised for many rows per sequence, where the work is a dense fp8
-// contraction (16384 flop per (row, key)) and the MFMA rate is the bound.
+// contraction (16384 flop per (row, key)).
 //
 // gfx950 design.
-//  * Workgroup = 16 query rows of one sequence x a chunk of 4096 keys; each of
+//  * Workgroup = 16 query rows of one sequence x a chunk of 8192 keys; each of
 //    the 8 waves owns two rows and keeps their q (64 heads x 128 e4m3 each) in
 //    registers as A operands of v_mfma_f32_32x32x64_f8f6f4 (M = 32 heads,
 //    N = 32 keys, K = 64; 4 instructions per row and 32 keys), the fastest
 //    fp8 shape on this chip.  One B-operand read of 32 keys feeds both rows.
 //  * The C layout gives each lane 16 heads of one key, so the weighted ReLU
 //    head sum is 32 in-lane FMAs (ReLU as one v_med3_f32) plus one lane swap
-//    (v_permlane32_swap).  This epilogue, two VALU operations per (row, key,
-//    head), costs about as much issue time as the MFMAs and bounds the kernel.
+//    (v_permlane32_swap): about 70 VALU operations per row and 32 keys, whose
+//    issue time (4 cycles each) exceeds the 4 MFMAs' 256 cycles.  The kernel
+//    is bound by VALU issue, and the schedule is built to overlap the two:
+//    the MFMAs of one row are interleaved (sched_group_barrier) with the
+//    epilogue of the other row's previous product.
 //  * K arrives in stages of 256 keys (four 64-token pages, located through the
 //    block table), copied global->LDS (global_load_lds_dwordx4, one whole
 //    128-byte key row per 8 lanes) into a double-buffered tile where key n's
 //    16-byte chunk c sits in slot c ^ ((n >> 1) & 7) of its row: the B-operand
 //    reads of 16 consecutive keys then hit distinct banks.  The copy of stage
 //    s + 1 is in flight while stage s is multiplied.
-//  * Workgroup ids run over the key chunks fastest, so the 8 XCDs each serve
-//    two key chunks from their own L2 to every row block.
+//  * Workgroup ids run over the key chunks fastest, so for a 65,536-key
+//    sequence each of the 8 XCDs serves one key chunk from its own L2 to every
+//    row block.
 //  * Per-row causal bound with an early exit: only the stages holding a key
-//    some row of the block can see are copied and multiplied; inside them
-//    keys s >= e_r are masked.  With clean_logits the rest of the chunk (to
-//    the logits stride) only gets -inf stores, so a block whose rows see a
-//    short prefix pays for its causal extent, not the whole rectangle.
-//    Chunks cover the whole logits stride, so no separate tail pass is needed.
+//    some row of the block can see are copied and multiplied; stores past a
+//    row's extent e_r fall outside its buffer range and are dropped.  With
+//    clean_logits each row's keys from e_r to the chunk end get -inf stores
+//    only, so a block whose rows see a short prefix pays for its causal
+//    extent, not the whole rectangle.  Chunks cover the whole logits stride,
+//    so no separate tail pass is needed.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,7 +47,7 @@ constexpr int kWavesPf = 8;
 constexpr int kRowsPerWave = 2;
 constexpr int kRowsPerBlock = kWavesPf * kRowsPerWave;   // 16 query rows per workgroup
 constexpr int kThreadsPf = 64 * kWavesPf;
-constexpr int kChunkKeys = 4096;                 // keys per workgroup
+constexpr int kChunkKeys = 8192;                 // keys per workgroup
 constexpr int kStageKeys = 256;                  // keys per LDS stage (four pages)
 constexpr int kPagesPerChunk = kChunkKeys / kPage;
 constexpr int kStageCodeBytes = kStageKeys * kIdxDim;    // 32 KB
@@ -135,14 +140,19 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
   // Physical pages of the chunk, lane p of every wave holding page p (-1:
   // none); a copy picks its page with readlane (a scalar, no LDS round trip).
   const int pages_b = (L + kPage - 1) / kPage;
-  int pg = -1;
-  {
-    const int j = kc * kPagesPerChunk + lane;
-    if (j < pages_b && lane < kPagesPerChunk) {
+  static_assert(kPagesPerChunk == 128, "two page registers");
+  int pg[2] = {-1, -1};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = kc * kPagesPerChunk + 64 * h + lane;
+    if (j < pages_b) {
       const int id = a.batch.block_table[(int64_t)b * a.batch.bt_stride + j];
-      pg = (id >= 0 && id < a.batch.num_pages) ? id : -1;
+      pg[h] = (id >= 0 && id < a.batch.num_pages) ? id : -1;
     }
   }
+  auto page_id = [&](int p) __attribute__((always_inline)) {   // p wave-uniform
+    return p < 64 ? __builtin_amdgcn_readlane(pg[0], p) : __builtin_amdgcn_readlane(pg[1], p - 64);
+  };
   const unsigned char* const zero_src = reinterpret_cast<const unsigned char*>(g_zero_kv);
 
   // Copy of stage st into buffer buf: wave w fills 1 KB blocks w * kDmaPerWave
@@ -152,7 +162,7 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
   // kPagesPerStage waves also copy one page's 256 scale bytes (lanes 0-15).
   auto copy_stage = [&](int st, int buf) __attribute__((always_inline)) {
     const uint32_t dst = lds_addr(sh.codes[buf]);
-    const int id = __builtin_amdgcn_readlane(pg, st * kPagesPerStage + (wave * kDmaPerWave * 8) / kPage);
+    const int id = page_id(st * kPagesPerStage + (wave * kDmaPerWave * 8) / kPage);
     const unsigned char* base = id >= 0 ? a.cache + (int64_t)id * a.page_stride : zero_src;
     // Key row n = 8 blk + l / 8 of the stage: swz(n) = (4 blk + l / 16) & 7 =
     // l / 16 + 4 (blk & 1), so the slot offsets take two per-lane values.
@@ -165,7 +175,7 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
       lds_dma16(base + off, dst + blk * 1024);
     }
     if (wave < kPagesPerStage) {
-      const int ids = __builtin_amdgcn_readlane(pg, st * kPagesPerStage + wave);
+      const int ids = page_id(st * kPagesPerStage + wave);
       const unsigned char* src = ids >= 0 ? a.cache + (int64_t)ids * a.page_stride + kIdxScaleOff : zero_src;
       if (lane < 16) lds_dma16(src + 16 * lane, lds_addr(&sh.scales[buf][kPage * wave]));
     }
@@ -230,64 +240,69 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
   const uint32_t lane_off = hb == 0 ? 4u * (uint32_t)nb : kDrop;
 
   // Epilogue of row j and the 32 keys at chunk offset kb + nb: weighted ReLU
-  // head sum (in-lane over the lane's 32 heads in two chains, then lanes 0-31
-  // add lanes 32-63 with one lane swap of the chains' sum held twice) times
-  // the K scale.
-  auto epi_value = [&](int j, const v16f* acc, float scale) __attribute__((always_inline)) {
-    float p0 = 0.f, p1 = 0.f;
+  // head sum (in-lane over the lane's 32 heads in one chain, head tile 0
+  // first, then lanes 0-31 add lanes 32-63 with one lane swap of the sum held
+  // twice) times the K scale.  Split in two parts so a half step can be cut
+  // into two scheduling regions.
+  auto epi_part = [&](int j, const v16f& acc_t, int mt, float p) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p0 = fmaf(ro[j].wr[0][i], relu_finite(acc[0][i]), p0);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p1 = fmaf(ro[j].wr[1][i], relu_finite(acc[1][i]), p1);
-    float x = p0 + p1, y = p0 + p1;
+    for (int i = 0; i < 16; ++i) p = fmaf(ro[j].wr[mt][i], relu_finite(acc_t[i]), p);
+    return p;
+  };
+  auto epi_finish = [&](float p, float scale) __attribute__((always_inline)) {
+    float x = p, y = p;
     asm volatile("" : "+v"(y));      // two registers, so the swap needs no copies
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
     return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * scale;
   };
+  auto epi_value = [&](int j, const v16f* acc, float scale) __attribute__((always_inline)) {
+    return epi_finish(epi_part(j, acc[1], 1, epi_part(j, acc[0], 0, 0.f)), scale);
+  };
   auto epi_store = [&](int j, float v, int kb) __attribute__((always_inline)) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), out_rsrc[j], lane_off + 4u * (uint32_t)kb, 0, 0);
   };
-  auto epilogue = [&](int j, const v16f* acc, float scale, int kb) __attribute__((always_inline)) {
-    epi_store(j, epi_value(j, acc, scale), kb);
-  };
 
-  // B operand (32 keys x 128 dims, this lane's slots) and K scale of one step.
+  // B operand (32 keys x 128 dims, this lane's slots, K half kh) and K scale
+  // of one step.
   v8i bop[2];
-  auto load_b = [&](int buf, int step, float& sc) __attribute__((always_inline)) {
+  auto load_b_half = [&](int buf, int step, int kh) __attribute__((always_inline)) {
     const unsigned char* tb = sh.codes[buf] + step * 32 * kIdxDim;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const v4i x0 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh]);
-      const v4i x1 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh + 1]);
-      bop[kh] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-    }
-    sc = sh.scales[buf][step * 32 + nb];
+    const v4i x0 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh]);
+    const v4i x1 = *reinterpret_cast<const v4i*>(tb + boff[2 * kh + 1]);
+    bop[kh] = v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
   };
-  auto mfma_row = [&](int j, v16f* acc) __attribute__((always_inline)) {
+  auto load_scale = [&](int buf, int step) __attribute__((always_inline)) { return sh.scales[buf][step * 32 + nb]; };
+  // Both head tiles of row j over K half kh.
+  auto mfma_half = [&](int j, int kh, v16f* acc) __attribute__((always_inline)) {
     v16f z;
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = 0.f;
-    acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[0][0], bop[0], z, 0, 0, 0, 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[1][0], bop[0], z, 0, 0, 0, 0, 0, 0);
-    acc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[0][1], bop[1], acc[0], 0, 0, 0, 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[1][1], bop[1], acc[1], 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ro[j].qa[mt][kh], bop[kh], kh == 0 ? z : acc[mt],
+                                                                0, 0, 0, 0, 0, 0);
   };
-  // Issue order of a half step: one MFMA per 19 VALU operations of the
-  // epilogue (76 in all); with `reload`, the next step's B operand is read
-  // into the same registers as soon as the MFMAs that use them have issued
-  // (K half 0 after the second MFMA, K half 1 and the scale after the fourth).
-  auto interleave = [&](bool reload) __attribute__((always_inline)) {
+  // Issue orders.  A half step without operand reads: one MFMA per ~18 VALU
+  // operations of the epilogue (70 in all).  A half step that reads the next
+  // step's operand: two regions, each an MFMA pair (both head tiles of one
+  // K half), then the LDS reads of that K half (into the registers the pair
+  // has just consumed), then half the epilogue.
+  auto order_plain = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto order_reload = [&](int nds) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (reload) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
-    __builtin_amdgcn_sched_barrier(0);    // nothing moves across half steps
+    if (nds == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Software pipeline over steps of 32 keys, two rows per wave: the MFMAs of
@@ -314,28 +329,43 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();            // stage st landed; buffer (st + 1) & 1 is free
     if (st + 1 < nstages) copy_stage(st + 1, buf ^ 1);
-    load_b(buf, 0, sc);
-    mfma_row(0, acc0);
-    epilogue(1, acc1, sc_prev, kb_prev);
+    load_b_half(buf, 0, 0);
+    load_b_half(buf, 0, 1);
+    sc = load_scale(buf, 0);
+    mfma_half(0, 0, acc0);
+    mfma_half(0, 1, acc0);
+    epi_store(1, epi_value(1, acc1, sc_prev), kb_prev);
     epi_store(1, held1, kb_held - 32);
     epi_store(0, held0, kb_held);
-    interleave(false);
+    order_plain();
 #pragma unroll
     for (int step = 0; step < kStageKeys / 32; ++step) {
       const int kb = st * kStageKeys + step * 32;
       const bool last = step + 1 == kStageKeys / 32;
       const float sc_cur = sc;
-      mfma_row(1, acc1);
-      if (!last) epilogue(0, acc0, sc_cur, kb);
-      else held0 = epi_value(0, acc0, sc_cur);
-      if (!last) load_b(buf, step + 1, sc);
-      interleave(!last);
       if (!last) {
-        mfma_row(0, acc0);
-        if (step + 2 < kStageKeys / 32) epilogue(1, acc1, sc_cur, kb);
-        else held1 = epi_value(1, acc1, sc_cur);
-        interleave(false);
+        // row 1's product beside row 0's epilogue, reading the next operand
+        mfma_half(1, 0, acc1);
+        load_b_half(buf, step + 1, 0);
+        const float p = epi_part(0, acc0[0], 0, 0.f);
+        order_reload(2);
+        mfma_half(1, 1, acc1);
+        load_b_half(buf, step + 1, 1);
+        sc = load_scale(buf, step + 1);
+        epi_store(0, epi_finish(epi_part(0, acc0[1], 1, p), sc_cur), kb);
+        order_reload(3);
+        // row 0's next product beside row 1's epilogue
+        mfma_half(0, 0, acc0);
+        mfma_half(0, 1, acc0);
+        const float v1 = epi_value(1, acc1, sc_cur);
+        if (step + 2 < kStageKeys / 32) epi_store(1, v1, kb);
+        else held1 = v1;
+        order_plain();
       } else {
+        mfma_half(1, 0, acc1);
+        mfma_half(1, 1, acc1);
+        held0 = epi_value(0, acc0, sc_cur);
+        order_plain();
         sc_prev = sc_cur;
         kb_prev = kb;
         kb_held = kb;
@@ -344,7 +374,7 @@ __global__ void __launch_bounds__(kThreadsPf) indexer_prefill_kernel(PrefillArgs
   }
   epi_store(1, held1, kb_held - 32);
   epi_store(0, held0, kb_held);
-  epilogue(1, acc1, sc_prev, kb_prev);
+  epi_store(1, epi_value(1, acc1, sc_prev), kb_prev);
 }
 
 }  // namespace
