@@ -309,11 +309,13 @@ __global__ void __launch_bounds__(64 * kWavesPg) indexer_paged_kernel(PagedArgs 
   };
 
   load_batch(p_begin);
-  // q of the first page's sequence goes out with the block-table load
-  set_seq(find_seq(s_pref, B, p_begin));
+  // the first pages' copies go out as soon as the block table is in, then
+  // the q rows of the first page's sequence (their latency hides behind the
+  // copies')
 #pragma unroll
   for (int i = 0; i < kRingPg; ++i)
     if (p_begin + i < p_end) issue(p_begin + i);
+  set_seq(find_seq(s_pref, B, p_begin));
   for (int p = p_begin; p < p_end; ++p) {
     // this page's copies; what was issued after them (the next pages' copies,
     // logit stores, any reload) may stay in flight
