@@ -89,7 +89,7 @@ def test_latent_cache_write_fp8_bit_exact(dsa, T, num_pages, lat_stride, rope_st
     assert bad.shape[0] == 0, f"{bad.shape[0]} bytes differ, first at page/byte {tuple(bad[0])}"
 
 
-@pytest.mark.parametrize("splits", [0, 1, 3, 16])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3, 12, 16, 32])
 @pytest.mark.parametrize("H", [16, 32, 48, 64, 80, 96, 112, 128])
 def test_sparse_mla_fp8_parity(dsa, H, splits):
     wl, batch, t, kv8, idx = mla8_inputs([3000, 700, 130, 2049], [1, 2, 1, 1], H, seed=H + splits)
