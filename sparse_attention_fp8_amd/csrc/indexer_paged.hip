@@ -62,7 +62,10 @@ __device__ __attribute__((aligned(16))) uint8_t g_zero_page[kPageLds] = {};
 
 struct PagedShared {
   unsigned char ring[kWavesPg][kRingPg][kPageLds];
-  int pref[DSA_MAX_SEQS + 1];
+  union {
+    int pref[DSA_MAX_SEQS + 1];             // more than 64 sequences: one prefix per workgroup
+    int wave_pref[kWavesPg][64 + 1];        // at most 64: a private prefix per wave
+  };
   int wave_tot[kWavesPg];
 };
 
@@ -179,12 +182,26 @@ __device__ __forceinline__ float page_row_logit(const QRow& qr, const v8i (&b)[2
 template <int QL>
 __global__ void __launch_bounds__(64 * kWavesPg) indexer_paged_kernel(PagedArgs a) {
   __shared__ PagedShared sh;
-  build_page_prefix(a.batch, sh.pref, sh.wave_tot);
-  const int* s_pref = sh.pref;
-
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int B = a.batch.num_seqs;
+  // Page prefix over the sequences.  With at most 64 sequences every wave
+  // builds its own with one wave scan (lane b: sequence b) into a private LDS
+  // copy -- no workgroup barrier between the kernel's start and its first
+  // block-table load; more sequences take the workgroup-wide build.
+  const int* s_pref;
+  if (B <= 64) {
+    const int pages = lane < B ? seq_pages(a.batch, lane) : 0;
+    const int incl = wave_inclusive_scan(pages);
+    int* wp = sh.wave_pref[wave];
+    if (lane < B) wp[lane] = incl - pages;
+    if (lane == 63) wp[B] = incl;     // lanes past B add nothing: lane 63 holds the total
+    s_pref = wp;
+  } else {
+    build_page_prefix(a.batch, sh.pref, sh.wave_tot);
+    s_pref = sh.pref;
+  }
+
   const int total = s_pref[B];
   const int64_t nw = (int64_t)gridDim.x * kWavesPg;
   const int64_t gw = (int64_t)blockIdx.x * kWavesPg + wave;

@@ -118,6 +118,8 @@ INDEXER_CASES = {
     "prefill_rows": ([2600], [200], {}),
     "prefill_chunks": ([9000, 5000, 64], [300, 17, 9], {}),
     "many_seqs": (list(range(1, 400, 7)), [1] * 57, {}),
+    # more than 64 sequences: the paged kernel's workgroup-wide page prefix
+    "over_64_seqs": ([(37 * i) % 700 + 1 for i in range(100)], [1 + (i % 3 == 0) for i in range(100)], {}),
 }
 
 
