@@ -532,13 +532,16 @@ __global__ void __launch_bounds__(kThreads) topk_rows64_kernel(TopkArgs a) {
   }
   Keys<32> k0;
   load_keys(k0, row, min(e, kChunk), lds.stage);
-  __syncthreads();   // every wave has read its keys: the staging area is free
   if (e <= kChunk) {
+    __syncthreads();   // every wave has read its keys: the staging area is free
     const Selection sel = radix_select(k0, k, sh);
     const int emitted = emit_selected(k0, sel, k, sh, [&](int pos, int i) { out[pos] = i; });
     for (int i = emitted + (int)threadIdx.x; i < k; i += kThreads) out[i] = -1;
     return;
   }
+  // Each wave stages both segments in its own region of the staging area, so
+  // its copy of segment 1 goes out as soon as it has read back segment 0,
+  // with no barrier between the two loads.
   Keys<32> k1;
   load_keys(k1, row + kChunk, e - kChunk, lds.stage);   // 128 KB in: kChunk * 4 bytes is 16-byte aligned
   __syncthreads();   // segment 1 read back; the selection state (zeroed by both loads) is visible
