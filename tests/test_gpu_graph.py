@@ -15,9 +15,17 @@ from test_gpu_parity import DEV, check_logits, check_mla, mla_oracle, oracle_ind
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("splits", [0, 1, 3])
-def test_step_graph_replays_match_eager(dsa, splits):
-    wl = synth.make_workload([2500, 130, 7000, 40000], [2, 1, 1, 1], 16, seed=11, spare_pages=4, poison=True)
+@pytest.mark.parametrize("mode,splits", [("paged", 0), ("paged", 1), ("paged", 3), ("prefill", 0), ("prefill", 2),
+                                        ("noalloc", 0), ("noalloc", 3)])
+def test_step_graph_replays_match_eager(dsa, mode, splits):
+    """mode: paged -- the decode step; prefill -- a chunked-prefill step (the
+    prefill indexer with clean logits, rows over two 8192-key chunks); noalloc
+    -- the decode step with the sparse MLA call that keeps its partials in the
+    library's static device array (the entry point for callers under capture)."""
+    if mode == "prefill":
+        wl = synth.make_workload([3000, 300, 9000], [150, 40, 20], 16, seed=13, spare_pages=4, poison=True)
+    else:
+        wl = synth.make_workload([2500, 130, 7000, 40000], [2, 1, 1, 1], 16, seed=11, spare_pages=4, poison=True)
     batch, t = to_dev(wl)
     R, H, k = wl.num_rows, wl.num_heads, wl.topk
     stride = (wl.max_seq_len + 3) // 4 * 4
@@ -29,11 +37,17 @@ def test_step_graph_replays_match_eager(dsa, splits):
     ws_mla = torch.empty(max(dsa.sparse_mla_workspace_bytes(batch, H, k, splits), 1), dtype=torch.uint8,
                          device=DEV)
 
+    indexer = dsa.indexer_logits_prefill if mode == "prefill" else dsa.indexer_logits_paged
+
     def step():
-        dsa.indexer_logits_paged(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=True)
+        indexer(batch, t["q_fp8"], t["weights"], t["idx_cache"], logits, clean_logits=True)
         dsa.topk(batch, logits, indices, k=k, workspace=ws_topk)
-        dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
-                              num_splits=splits, workspace=ws_mla)
+        if mode == "noalloc":
+            dsa.sparse_mla_decode_noalloc(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
+                                          num_splits=splits)
+        else:
+            dsa.sparse_mla_decode(batch, t["q_mla"], t["kv_cache"], indices, wl.softmax_scale, out, lse,
+                                  num_splits=splits, workspace=ws_mla)
 
     step()
     torch.cuda.synchronize()
