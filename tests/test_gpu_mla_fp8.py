@@ -10,7 +10,7 @@ import torch
 import oracle
 from sparse_attention_fp8_amd import synth
 
-from test_gpu_parity import DEV, check_logits, check_mla, oracle_indexer, run_indexer, run_topk, to_dev
+from test_gpu_parity import DEV, check_logits, check_mla, oracle_indexer, rising_scores, run_indexer, run_topk, to_dev
 from test_gpu_quant import slots_for
 
 pytestmark = pytest.mark.gpu
@@ -109,6 +109,25 @@ def test_sparse_mla_fp8_parity_other_k(dsa, H, k, splits):
     out, lse = run_mla8(dsa, wl, batch, t, idx, splits)
     o_ref, l_ref = mla8_oracle(wl, kv8, idx)
     check_mla(out, lse, o_ref, l_ref, f"fp8 H={H} k={k} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_sparse_mla_fp8_rising_scores_rescale(dsa, H, splits):
+    """Scores that climb tile by tile (the rope keys grow with the selection
+    position), so the accumulators are rescaled in the middle of a split."""
+    wl = synth.make_workload([5000, 3000], [1, 2], H, seed=91 + H, spare_pages=4, poison=True)
+    _, ext = oracle.row_extents(wl.seq_lens.numpy(), wl.query_start.numpy())
+    rng = np.random.default_rng(H + 1)
+    idx = np.stack([oracle.topk_row(rng.normal(size=max(int(e), 1)), int(e), 2048) for e in ext])
+    rising_scores(wl, idx)
+    batch, t = to_dev(wl)
+    kv8 = kv8_of(wl)
+    t["kv8"] = torch.from_numpy(kv8).to(DEV)
+    out, lse = run_mla8(dsa, wl, batch, t, idx, splits)
+    o_ref, l_ref = mla8_oracle(wl, kv8, idx)
+    assert l_ref[0].min() > 60.0
+    check_mla(out, lse, o_ref, l_ref, f"H={H} splits={splits}")
 
 
 def test_sparse_mla_fp8_padded_pages_masked_and_empty_rows(dsa):

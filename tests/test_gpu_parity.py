@@ -447,6 +447,40 @@ def test_sparse_mla_parity_other_k(dsa, H, k, splits):
     check_mla(out, lse, o_ref, l_ref, f"H={H} k={k} splits={splits}")
 
 
+def rising_scores(wl, idx, row=0):
+    """Make row `row`'s scores climb with the selection position: every head's
+    rope q becomes 0.5 and the rope part of the key at position p of the row's
+    list becomes p // 64, so each 64-key tile adds about 2.3 to the scores
+    (scale 1/sqrt(192)).  The running maximum then passes its lazy-rescale
+    margin every few tiles.  The latent (value) part is left as it is."""
+    wl.q_mla[row, :, 512:] = 0.5
+    b = int(np.searchsorted(wl.query_start.numpy(), row, side="right")) - 1
+    toks = idx[row][idx[row] >= 0].astype(np.int64)
+    pos = np.nonzero(idx[row] >= 0)[0]
+    pages = wl.block_table[b].numpy().astype(np.int64)[toks // 64]
+    kv = wl.kv_cache.view(-1)
+    base = torch.from_numpy(pages * wl.kv_cache.shape[1] + (toks % 64) * 576 + 512)
+    cols = base[:, None] + torch.arange(64)[None, :]
+    kv[cols.reshape(-1)] = torch.from_numpy(np.repeat((pos // 64).astype(np.float32), 64)).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("H", [16, 32, 48, 64, 128])
+def test_sparse_mla_rising_scores_rescale(dsa, H, splits):
+    """Scores that climb tile by tile, so the accumulators are rescaled in the
+    middle of a split (random scores almost never move the maximum that far)."""
+    wl = synth.make_workload([5000, 3000], [1, 2], H, seed=90 + H, spare_pages=4, poison=True)
+    _, ext = oracle.row_extents(wl.seq_lens.numpy(), wl.query_start.numpy())
+    rng = np.random.default_rng(H)
+    idx = np.stack([oracle.topk_row(rng.normal(size=max(int(e), 1)), int(e), 2048) for e in ext])
+    rising_scores(wl, idx)
+    batch, t = to_dev(wl)
+    out, lse = run_mla(dsa, wl, batch, t, idx, splits)
+    o_ref, l_ref = mla_oracle(wl, idx)
+    assert l_ref[0].min() > 60.0        # the climb happened (the last tile scores about 70)
+    check_mla(out, lse, o_ref, l_ref, f"H={H} splits={splits}")
+
+
 def test_sparse_mla_masked_duplicate_and_invalid_entries(dsa):
     wl, batch, t, idx = mla_inputs(dsa, [5000, 600], [1, 2], 16, seed=77)
     idx = idx.copy()
