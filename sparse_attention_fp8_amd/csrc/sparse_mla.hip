@@ -92,9 +92,10 @@ struct MlaShared {
 // operand takes 72 VGPRs), but a PV wave can take PVH head tiles over fewer
 // dims, so that each transposed V^T read feeds PVH MFMAs.  With four head
 // tiles the QK and PV phases both run at the LDS bandwidth (operand reads
-// plus the next tile's copy); PVH = 4 reads V^T once per tile (eight waves
-// of 64 dims each; 0.8 % faster than two head tiles over 128 dims at 64
-// heads over 128 rows, the accumulators taking the same 64 registers).
+// plus the next tile's copy).  The 16- and 32-head blocks launched below use
+// PVH = 1; 64-head blocks go to the wave-specialised kernel further down
+// (with this kernel, PVH = 4 -- V^T read once per tile by eight waves of 64
+// dims -- was its best form).
 template <int HT, int TP, bool DEEP, int PVH>
 __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   constexpr int NW = HT * TP;          // waves
@@ -468,6 +469,375 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 64-head blocks, wave-specialised.  Waves 0-3 score (wave w: head tile w
+// over all tokens of a tile), waves 4-7 multiply (wave 4 + d: dims
+// 128 d .. 128 d + 127 of all four head tiles).  Tiles are 32 tokens in a
+// ring of four LDS buffers: in iteration i the scorers run QK and the softmax
+// of tile i and copy tile i + 2 while the PV waves accumulate tile i - 1, and
+// one barrier ends the iteration.  Each SIMD holds one scoring and one PV
+// wave, so the softmax's VALU work overlaps the other wave's MFMAs; a
+// scorer holds all tokens of its head tile, so the tile maximum needs no
+// exchange; and each V^T read feeds four MFMAs.  Measured against the
+// eight-wave kernel above at 64 heads over 128 rows (k = 2048): 5.5 % fewer
+// cycles.  What bounds it: the scorers' C-operand reads (each head tile reads
+// the whole tile) run at the LDS bandwidth, and the softmax and the LDS
+// round trip of its stores before the barrier follow them serially.
+constexpr int kTileW = 32;                            // tokens per tile
+constexpr int kRgW = kTileW / 8;                      // row groups per tile
+constexpr int kTileBytesW = kTileW * kChunks * 16;    // 36864
+constexpr int kBufW = 4;                              // tile buffers
+constexpr int kPairSlots = 8;                         // ring of 64-entry index / table slots
+constexpr int kQkAheadW = 4;                          // C-operand reads in flight in QK
+constexpr int kPvAheadW = 2;                          // V^T reads in flight in PV
+
+// Small arrays first: one per-lane base register plus 16-bit offsets reaches them.
+struct WsShared {
+  uint2 p[2][4][2][4][16];          // bf16 probabilities [tile & 1][head tile][token tile][g][head]
+  float alpha[2][64];               // rescale factor of each head for tile & 1
+  int resc[2][4];                   // scorer w moved the reference max of some head in tile & 1
+  float m[64];                      // final reference max of each head (log2 domain)
+  float l[64];                      // final row sum of each head
+  int idx[kPairSlots][64];          // indices of tiles 2P, 2P + 1 in slot P % 8
+  int page[kPairSlots][64];         // their block-table entries
+  unsigned char tile[kBufW][kTileBytesW];   // gathered rows (1 KB blocks as above, 4 row groups)
+};
+
+__global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
+  constexpr int ND = kChunkGroups;        // copies per scorer and tile (its row group, 9 column groups)
+  constexpr int NDT = 8;                  // 16-dim tiles per PV wave
+  __shared__ WsShared sh;
+
+  const int R = a.batch.num_rows;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n16 = lane & 15;
+  const int bid = blockIdx.x;
+  const int q8 = bid >> 3;
+  const int hb = q8 % a.head_blocks;
+  const int rest = (q8 / a.head_blocks) * 8 + (bid & 7);
+  if (rest >= R * a.splits) return;
+  const int r = rest / a.splits;
+  const int sp = rest % a.splits;
+  const int hbase = hb * 64;
+  const bool scorer = wave < 4;
+  const int w4 = wave & 3;
+
+  const int slot0 = sp * a.split_slots;
+  const int slot1 = min(slot0 + a.split_slots, a.k);
+  const int ntiles = (slot1 - slot0 + kTileW - 1) / kTileW;
+
+  // Row pointers: the indices of tile pair P (64 slots) are copied into ring
+  // slot P % 8 of sh.idx, then their block-table entries into sh.page (wave 0
+  // for pairs 0-3 before the loop, PV wave 4 inside it, so no scorer waits
+  // for those round trips).
+  const int32_t* idx_row = a.indices + (int64_t)r * a.k;
+  int bc = 0, e = 0;
+  auto issue_idx = [&](int P) {
+    const int j = min(slot0 + P * 64 + lane, slot1 - 1);
+    lds_dma4(idx_row + j, lds_addr(sh.idx[P & 7]));
+  };
+  auto issue_page = [&](int P) {
+    const int idx = sh.idx[P & 7][lane];
+    const int ic = (idx >= 0 && idx < a.batch.max_seq_len) ? idx : 0;
+    lds_dma4(a.batch.block_table + (int64_t)bc * a.batch.bt_stride + (ic >> 6), lds_addr(sh.page[P & 7]));
+  };
+  auto row_src = [&](int t, int tok, bool& valid) -> const unsigned char* {
+    const int o = (t & 1) * kTileW + tok;
+    const int idx = sh.idx[(t >> 1) & 7][o];
+    const int page = sh.page[(t >> 1) & 7][o];
+    valid = slot0 + t * kTileW + tok < slot1 && idx >= 0 && idx < e && page >= 0 && page < a.batch.num_pages;
+    return valid ? reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page * a.kv_stride + (idx & 63) * kKvDim)
+                 : reinterpret_cast<const unsigned char*>(g_zero_row);
+  };
+  auto tile_mask = [&](int t) -> uint32_t {
+    bool v;
+    row_src(t, lane & 31, v);
+    return (uint32_t)__ballot(v);
+  };
+  // Scorer w copies row group w of tile t: lane l takes slot l & 7 of row 8 w + l / 8.
+  auto gather_src = [&](int t) -> const unsigned char* {
+    bool v;
+    return row_src(t, 8 * w4 + (lane >> 3), v) + (((lane & 7) ^ (lane >> 3)) << 4);
+  };
+  auto gather_dst = [&](int t) -> uint32_t { return lds_addr(sh.tile[t & 3]) + w4 * 1024; };
+
+  if (wave == 0 && ntiles > 0) {
+#pragma unroll
+    for (int P = 0; P < 4; ++P) issue_idx(P);
+  }
+  {
+    int b;
+    seq_and_extent_wave(a.batch, r, b, e);
+    bc = b >= 0 ? b : 0;
+  }
+
+  if (scorer) {
+    // ------------------------------------------------------------ scorers
+    const int ht = w4;
+    const int hq = hbase + ht * 16 < a.H ? hbase + ht * 16 + n16 : hbase + n16;
+    uint4 qreg[18];
+    {
+      const uint16_t* qp = a.q + ((int64_t)r * a.H + hq) * kKvDim + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+    }
+    wait_vmcnt<0>();
+    if (wave == 0 && ntiles > 0) {
+#pragma unroll
+      for (int P = 0; P < 3; ++P) issue_page(P);
+      wait_vmcnt<0>();
+    }
+    __syncthreads();                                     // B_pre0: pairs 0-2 visible
+    if (ntiles > 0) {
+      const unsigned char* src = gather_src(0);
+      const uint32_t dst = gather_dst(0);
+#pragma unroll
+      for (int cg = 0; cg < ND; ++cg) lds_dma16(src + cg * 128, dst + cg * (kRgW * 1024));
+    }
+    if (ntiles > 1) {
+      const unsigned char* src = gather_src(1);
+      const uint32_t dst = gather_dst(1);
+#pragma unroll
+      for (int cg = 0; cg < ND; ++cg) lds_dma16(src + cg * 128, dst + cg * (kRgW * 1024));
+      wait_vmcnt<ND>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();                                     // B_pre1: tile 0 landed
+
+    const int r8 = n16 & 7;
+    const int qk0 = (n16 >> 3) * 1024 + r8 * 128 + ((g ^ r8) << 4);
+    float m_run = kMaskSentinel;
+    float l_part = 0.f;
+    // The index-ring entries of the next iteration's mask (tile i + 1) and
+    // copy (tile i + 3) are read at the top of iteration i and used at its
+    // end: an LDS read right after the barrier waits behind every wave's
+    // operand traffic (~800 cycles).  Table entries of tile t are visible
+    // from iteration t - 3 on.
+    const unsigned char* zero = reinterpret_cast<const unsigned char*>(g_zero_row);
+    uint32_t mask_n = ntiles > 0 ? tile_mask(0) : 0u;
+    const unsigned char* gsrc_n = 2 < ntiles ? gather_src(2) : zero;
+    for (int i = 0; i <= ntiles; ++i) {
+      const bool more = i + 2 < ntiles;
+      if (i < ntiles) {
+        const uint32_t mask = mask_n;
+        const unsigned char* gsrc = gsrc_n;
+        // raw ring entries for the next iteration
+        const int om = ((i + 1) & 1) * kTileW + (lane & 31);
+        const int idx_m = sh.idx[((i + 1) >> 1) & 7][om];
+        const int page_m = sh.page[((i + 1) >> 1) & 7][om];
+        const int og = ((i + 3) & 1) * kTileW + 8 * w4 + (lane >> 3);
+        const int idx_g = sh.idx[((i + 3) >> 1) & 7][og];
+        const int page_g = sh.page[((i + 3) >> 1) & 7][og];
+        asm volatile("" ::: "memory");   // issue those reads here, ahead of the QK operand reads
+        const uint32_t gdst = gather_dst(i + 2);
+        const int sl = i & 1;
+        v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+        if (mask != 0u) {
+          const unsigned char* tile = sh.tile[i & 3];
+          // step q: token tile q & 1, k-step q >> 1; copies on every fourth step
+          auto c_operand = [&](int q) __attribute__((always_inline)) {
+            const int tt = q & 1, ks = q >> 1;
+            return *reinterpret_cast<const uint4*>(tile + (qk0 ^ ((ks & 1) << 6)) + (ks >> 1) * (kRgW * 1024) +
+                                                   tt * 2048);
+          };
+          uint4 cr[kQkAheadW + 1];
+#pragma unroll
+          for (int q = 0; q < kQkAheadW; ++q) cr[q] = c_operand(q);
+#pragma unroll
+          for (int q = 0; q < 36; ++q) {
+            if (q + kQkAheadW < 36) cr[(q + kQkAheadW) % (kQkAheadW + 1)] = c_operand(q + kQkAheadW);
+            if ((q & 3) == 0 && more) lds_dma16(gsrc + (q >> 2) * 128, gdst + (q >> 2) * (kRgW * 1024));
+            s[q & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(cr[q % (kQkAheadW + 1)]),
+                                                              as_v8bf(qreg[q >> 1]), s[q & 1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if (more) {
+#pragma unroll
+          for (int cg = 0; cg < ND; ++cg) lds_dma16(gsrc + cg * 128, gdst + cg * (kRgW * 1024));
+        }
+        // softmax of head tile ht over the tile's 32 tokens (token 16 tt + 4 g + j in s[tt][j])
+        float tmax = kMaskSentinel;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool v = (mask >> (16 * tt + 4 * g + j)) & 1u;
+            const float z = v ? s[tt][j] * a.scale_log2 : kMaskSentinel;
+            s[tt][j] = z;
+            tmax = fmaxf(tmax, z);
+          }
+        tmax = fmaxf(tmax, lane_xor16(tmax));
+        tmax = fmaxf(tmax, lane_xor32(tmax));
+        float alpha;
+        const bool rescale = lazy_max_advance(m_run, tmax, alpha);
+        float psum = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          float pv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool v = (mask >> (16 * tt + 4 * g + j)) & 1u;
+            pv[j] = v ? __builtin_amdgcn_exp2f(s[tt][j] - m_run) : 0.f;
+            psum += pv[j];
+          }
+          v4bf16 b4;
+          b4[0] = (__bf16)pv[0]; b4[1] = (__bf16)pv[1]; b4[2] = (__bf16)pv[2]; b4[3] = (__bf16)pv[3];
+          uint2 pk;
+          __builtin_memcpy(&pk, &b4, 8);
+          sh.p[sl][ht][tt][g][n16] = pk;
+        }
+        l_part = l_part * alpha + psum;
+        if (g == 0) sh.alpha[sl][ht * 16 + n16] = alpha;
+        const bool any = __ballot(rescale) != 0ull;
+        if (lane == 0) sh.resc[sl][ht] = any ? 1 : 0;
+        {
+          const int t = i + 1;
+          const bool v = t < ntiles && slot0 + t * kTileW + (lane & 31) < slot1 && idx_m >= 0 && idx_m < e &&
+                         page_m >= 0 && page_m < a.batch.num_pages;
+          mask_n = (uint32_t)__ballot(v);
+        }
+        {
+          const int t = i + 3;
+          const int tok = 8 * w4 + (lane >> 3);
+          const bool v = t < ntiles && slot0 + t * kTileW + tok < slot1 && idx_g >= 0 && idx_g < e &&
+                         page_g >= 0 && page_g < a.batch.num_pages;
+          gsrc_n = (v ? reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page_g * a.kv_stride +
+                                                             (idx_g & 63) * kKvDim)
+                      : zero) +
+                   (((lane & 7) ^ (lane >> 3)) << 4);
+        }
+      }
+      // this wave's copies of tile i + 1 (issued one iteration ago) have landed
+      if (more) wait_vmcnt<ND>();
+      else wait_vmcnt<0>();
+      __syncthreads();                                   // B_i
+    }
+    const float l_own = l_part + lane_xor16(l_part);
+    const float l_sum = l_own + lane_xor32(l_own);
+    if (g == 0) {
+      sh.m[ht * 16 + n16] = m_run;
+      sh.l[ht * 16 + n16] = l_sum;
+    }
+    __syncthreads();                                     // B_end
+  } else {
+    // ------------------------------------------------------------ PV waves
+    __syncthreads();                                     // B_pre0
+    __syncthreads();                                     // B_pre1
+    const int d_base = w4 * 128;
+    const int pv_Lt = ((n16 >> 1) & 1) ^ (((g & 1) << 2) | (n16 >> 2));
+    const int pv_lane = (g >> 1) * 1024 + (((g & 1) << 2) + (n16 >> 2)) * 128 + 8 * (n16 & 1);
+    const int pv_part = (d_base >> 6) * (kRgW * 1024);
+    v4f acc[4][NDT];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    int idx_p = 0, page_p = -1;          // ring entries of tile i - 1, read one iteration ahead
+    for (int i = 0; i <= ntiles; ++i) {
+      // wave 4 keeps the index ring going: in odd iterations the table
+      // entries of pair (i + 5) / 2 (first read in iteration i + 3) and the
+      // indices of pair (i + 7) / 2; waited for by the next iteration's end
+      const bool ring = wave == 4 && (i & 1) && ((i + 5) >> 1) * 2 < ntiles;
+      if (ring) {
+        issue_page((i + 5) >> 1);
+        issue_idx((i + 7) >> 1);
+      }
+      const int om = (i & 1) * kTileW + (lane & 31);
+      const int idx_c = sh.idx[(i >> 1) & 7][om];
+      const int page_c = sh.page[(i >> 1) & 7][om];
+      asm volatile("" ::: "memory");
+      if (i >= 1) {
+        const int j = i - 1;
+        const bool v = slot0 + j * kTileW + (lane & 31) < slot1 && idx_p >= 0 && idx_p < e && page_p >= 0 &&
+                       page_p < a.batch.num_pages;
+        const uint32_t mask = (uint32_t)__ballot(v);
+        if (mask != 0u) {
+          const int sl = j & 1;
+          if ((sh.resc[sl][0] | sh.resc[sl][1] | sh.resc[sl][2] | sh.resc[sl][3]) != 0) {
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+              const float al = sh.alpha[sl][ht * 16 + n16];
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] *= al;
+            }
+          }
+          v8bf pb[4];
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) {
+            const uint2 p0 = sh.p[sl][ht][0][g][n16];
+            const uint2 p1 = sh.p[sl][ht][1][g][n16];
+            pb[ht] = as_v8bf(make_uint4(p0.x, p0.y, p1.x, p1.y));
+          }
+          const unsigned char* pv_base = sh.tile[j & 3] + pv_part + pv_lane;
+          auto v_operand = [&](int dt) __attribute__((always_inline)) {
+            const unsigned char* vb = pv_base + (dt >> 2) * (kRgW * 1024) + ((pv_Lt ^ (2 * (dt & 3))) << 4);
+            const v4s lo = lds_read_tr16(vb);
+            const v4s hi = lds_read_tr16(vb + 2048);
+            const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            v8bf va;
+            __builtin_memcpy(&va, &vv, 16);
+            return va;
+          };
+          v8bf vr[kPvAheadW + 1];
+#pragma unroll
+          for (int dt = 0; dt < kPvAheadW; ++dt) vr[dt] = v_operand(dt);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+            if (dt + kPvAheadW < NDT) vr[(dt + kPvAheadW) % (kPvAheadW + 1)] = v_operand(dt + kPvAheadW);
+            const v8bf va = vr[dt % (kPvAheadW + 1)];
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+              acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ht], acc[ht][dt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      idx_p = idx_c;
+      page_p = page_c;
+      if (ring) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+      __syncthreads();                                   // B_i
+    }
+    __syncthreads();                                     // B_end: m and l of every head
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      if (hbase + ht * 16 >= a.H) continue;              // a missing head tile
+      const int hp = hbase + ht * 16 + n16;
+      const float l_tot = sh.l[ht * 16 + n16];
+      const float m_fin = sh.m[ht * 16 + n16];
+      if (a.splits == 1) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* op = a.out + ((int64_t)r * a.H + hp) * kVDim + d_base + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const v4f o = acc[ht][dt];
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
+          pk.y = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
+          *reinterpret_cast<uint2*>(op + dt * 16) = pk;
+        }
+        if (w4 == 0 && g == 0)
+          a.lse[(int64_t)r * a.H + hp] = l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t base = ((int64_t)sp * R + r) * a.H + hp;
+        float* pa = a.part_acc + base * kVDim + d_base + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const v4f o = acc[ht][dt];
+          *reinterpret_cast<float4*>(pa + dt * 16) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+        if (w4 == 0 && g == 0) {
+          a.part_ml[base * 2] = l_tot > 0.f ? m_fin : kMaskSentinel;
+          a.part_ml[base * 2 + 1] = l_tot;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 MlaPlan plan_sparse_mla(int num_rows, int max_seq_len, int H, int k, int num_splits, int num_cus) {
@@ -532,7 +902,7 @@ hipError_t launch_sparse_mla(const BatchArgs& batch, const uint16_t* q, int H, c
   } else if (H == 32) {
     hipLaunchKernelGGL((sparse_mla_kernel<2, 2, false, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((sparse_mla_kernel<4, 2, false, 4>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(sparse_mla_ws_kernel, dim3((unsigned)grid), dim3(512), 0, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
