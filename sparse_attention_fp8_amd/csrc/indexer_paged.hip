@@ -190,8 +190,16 @@ __global__ void __launch_bounds__(64 * kWavesPg) indexer_paged_kernel(PagedArgs 
   // copy -- no workgroup barrier between the kernel's start and its first
   // block-table load; more sequences take the workgroup-wide build.
   const int* s_pref;
+  // with at most 64 sequences lane b also keeps sequence b's row range and
+  // length, so switching sequences needs no memory round trip
+  int sq0 = 0, sq1 = 0, sL = 0;
   if (B <= 64) {
-    const int pages = lane < B ? seq_pages(a.batch, lane) : 0;
+    if (lane < B) {
+      sq0 = a.batch.query_start[lane];
+      sq1 = a.batch.query_start[lane + 1];
+      sL = clamp_len(a.batch.seq_lens[lane], a.batch.max_seq_len);
+    }
+    const int pages = lane < B && sq1 > sq0 ? (sL + kPage - 1) / kPage : 0;
     const int incl = wave_inclusive_scan(pages);
     int* wp = sh.wave_pref[wave];
     if (lane < B) wp[lane] = incl - pages;
@@ -254,12 +262,19 @@ __global__ void __launch_bounds__(64 * kWavesPg) indexer_paged_kernel(PagedArgs 
   // once here.
   auto set_seq = [&](int b) {
     cur_b = b;
-    q0 = a.batch.query_start[b];
-    const int q1 = a.batch.query_start[b + 1];
+    int q1;
+    if (B <= 64) {
+      q0 = __builtin_amdgcn_readlane(sq0, b);
+      q1 = __builtin_amdgcn_readlane(sq1, b);
+      L = __builtin_amdgcn_readlane(sL, b);
+    } else {
+      q0 = a.batch.query_start[b];
+      q1 = a.batch.query_start[b + 1];
+      L = clamp_len(a.batch.seq_lens[b], a.batch.max_seq_len);
+    }
     q_len = q1 - q0;
     row0 = max(q0, 0);
     nrows = min(q1, a.batch.num_rows) - row0;
-    L = clamp_len(a.batch.seq_lens[b], a.batch.max_seq_len);
     if (nrows <= QL) {
 #pragma unroll
       for (int jj = 0; jj < QL; ++jj)
