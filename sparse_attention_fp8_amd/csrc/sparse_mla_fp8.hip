@@ -290,9 +290,11 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
 #pragma unroll
         for (int st = 0; st < 10; ++st) {
           const int q = u * 10 + st;
+          if constexpr (HT < 4) {
 #pragma unroll
-          for (int i = 0; i < ND; ++i)
-            if (i * NQ / ND == q && pre) gather_one(gsrc, gssrc, gdst, i);
+            for (int i = 0; i < ND; ++i)
+              if (i * NQ / ND == q && pre) gather_one(gsrc, gssrc, gdst, i);
+          }
           if (st < 8) {
             const int cg = st >> 1;
             const uint4 raw = *reinterpret_cast<const uint4*>(tile + tile_off(cg, tok, 4 * (st & 1) + g));
@@ -381,6 +383,15 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
       if (__ballot(rescale) != 0ull) {                 // rare: a head's maximum moved up
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      }
+      // At 64-head blocks the next copy goes out after the softmax instead of
+      // between the QK steps (GRBM cycles at 64 heads over 128 rows -3.2 %; at
+      // 16 heads it costs 6 %, so smaller blocks keep the spread copies).
+      if constexpr (HT >= 4) {
+        if (pre) {
+#pragma unroll
+          for (int i = 0; i < ND; ++i) gather_one(gsrc, gssrc, gdst, i);
+        }
       }
       __syncthreads();                                 // P' of all token tiles
 
