@@ -474,15 +474,18 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 // over all tokens of a tile), waves 4-7 multiply (wave 4 + d: dims
 // 128 d .. 128 d + 127 of all four head tiles).  Tiles are 32 tokens in a
 // ring of four LDS buffers: in iteration i the scorers run QK and the softmax
-// of tile i and copy tile i + 2 while the PV waves accumulate tile i - 1, and
-// one barrier ends the iteration.  Each SIMD holds one scoring and one PV
+// of tile i while the PV waves accumulate tile i - 1 and then copy tile i + 2,
+// and one barrier ends the iteration.  Each SIMD holds one scoring and one PV
 // wave, so the softmax's VALU work overlaps the other wave's MFMAs; a
 // scorer holds all tokens of its head tile, so the tile maximum needs no
 // exchange; and each V^T read feeds four MFMAs.  Measured against the
-// eight-wave kernel above at 64 heads over 128 rows (k = 2048): 5.5 % fewer
-// cycles.  What bounds it: the scorers' C-operand reads (each head tile reads
-// the whole tile) run at the LDS bandwidth, and the softmax and the LDS
-// round trip of its stores before the barrier follow them serially.
+// eight-wave kernel above at 64 heads over 128 rows (k = 2048): 10.6 % fewer
+// cycles, of which 3.7 % come from the copies being issued by the PV waves
+// after their products (by the scorers inside or after the QK loop, or by the
+// PV waves before their products, it costs 2-6 %).  What bounds
+// it: the scorers' C-operand reads (each head tile reads the whole tile) run
+// at the LDS bandwidth, and the softmax and the LDS round trip of its stores
+// before the barrier follow them serially.
 constexpr int kTileW = 32;                            // tokens per tile
 constexpr int kRgW = kTileW / 8;                      // row groups per tile
 constexpr int kTileBytesW = kTileW * kChunks * 16;    // 36864
@@ -556,7 +559,7 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
     row_src(t, lane & 31, v);
     return (uint32_t)__ballot(v);
   };
-  // Scorer w copies row group w of tile t: lane l takes slot l & 7 of row 8 w + l / 8.
+  // Copies of tile t: wave 4 + w takes row group w (lane l: slot l & 7 of row 8 w + l / 8).
   auto gather_src = [&](int t) -> const unsigned char* {
     bool v;
     return row_src(t, 8 * w4 + (lane >> 3), v) + (((lane & 7) ^ (lane >> 3)) << 4);
@@ -590,49 +593,25 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
       wait_vmcnt<0>();
     }
     __syncthreads();                                     // B_pre0: pairs 0-2 visible
-    if (ntiles > 0) {
-      const unsigned char* src = gather_src(0);
-      const uint32_t dst = gather_dst(0);
-#pragma unroll
-      for (int cg = 0; cg < ND; ++cg) lds_dma16(src + cg * 128, dst + cg * (kRgW * 1024));
-    }
-    if (ntiles > 1) {
-      const unsigned char* src = gather_src(1);
-      const uint32_t dst = gather_dst(1);
-#pragma unroll
-      for (int cg = 0; cg < ND; ++cg) lds_dma16(src + cg * 128, dst + cg * (kRgW * 1024));
-      wait_vmcnt<ND>();
-    } else {
-      wait_vmcnt<0>();
-    }
     __syncthreads();                                     // B_pre1: tile 0 landed
 
     const int r8 = n16 & 7;
     const int qk0 = (n16 >> 3) * 1024 + r8 * 128 + ((g ^ r8) << 4);
     float m_run = kMaskSentinel;
     float l_part = 0.f;
-    // The index-ring entries of the next iteration's mask (tile i + 1) and
-    // copy (tile i + 3) are read at the top of iteration i and used at its
-    // end: an LDS read right after the barrier waits behind every wave's
-    // operand traffic (~800 cycles).  Table entries of tile t are visible
-    // from iteration t - 3 on.
-    const unsigned char* zero = reinterpret_cast<const unsigned char*>(g_zero_row);
+    // The index-ring entries of the next iteration's mask (tile i + 1) are
+    // read at the top of iteration i and used at its end: an LDS read right
+    // after the barrier waits behind every wave's operand traffic (~800
+    // cycles).  Table entries of tile t are visible from iteration t - 3 on.
     uint32_t mask_n = ntiles > 0 ? tile_mask(0) : 0u;
-    const unsigned char* gsrc_n = 2 < ntiles ? gather_src(2) : zero;
     for (int i = 0; i <= ntiles; ++i) {
-      const bool more = i + 2 < ntiles;
       if (i < ntiles) {
         const uint32_t mask = mask_n;
-        const unsigned char* gsrc = gsrc_n;
         // raw ring entries for the next iteration
         const int om = ((i + 1) & 1) * kTileW + (lane & 31);
         const int idx_m = sh.idx[((i + 1) >> 1) & 7][om];
         const int page_m = sh.page[((i + 1) >> 1) & 7][om];
-        const int og = ((i + 3) & 1) * kTileW + 8 * w4 + (lane >> 3);
-        const int idx_g = sh.idx[((i + 3) >> 1) & 7][og];
-        const int page_g = sh.page[((i + 3) >> 1) & 7][og];
         asm volatile("" ::: "memory");   // issue those reads here, ahead of the QK operand reads
-        const uint32_t gdst = gather_dst(i + 2);
         const int sl = i & 1;
         v4f s[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
         if (mask != 0u) {
@@ -689,33 +668,14 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
         if (g == 0) sh.alpha[sl][ht * 16 + n16] = alpha;
         const bool any = __ballot(rescale) != 0ull;
         if (lane == 0) sh.resc[sl][ht] = any ? 1 : 0;
-        // the next-but-one tile's copy goes out here, after the products and the
-        // softmax: issued inside the QK loop its copies cost the loop 1.9 %,
-        // before it 2 % more (GRBM cycles, 64 heads over 128 rows)
-        if (more) {
-#pragma unroll
-          for (int cg = 0; cg < ND; ++cg) lds_dma16(gsrc + cg * 128, gdst + cg * (kRgW * 1024));
-        }
         {
           const int t = i + 1;
           const bool v = t < ntiles && slot0 + t * kTileW + (lane & 31) < slot1 && idx_m >= 0 && idx_m < e &&
                          page_m >= 0 && page_m < a.batch.num_pages;
           mask_n = (uint32_t)__ballot(v);
         }
-        {
-          const int t = i + 3;
-          const int tok = 8 * w4 + (lane >> 3);
-          const bool v = t < ntiles && slot0 + t * kTileW + tok < slot1 && idx_g >= 0 && idx_g < e &&
-                         page_g >= 0 && page_g < a.batch.num_pages;
-          gsrc_n = (v ? reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page_g * a.kv_stride +
-                                                             (idx_g & 63) * kKvDim)
-                      : zero) +
-                   (((lane & 7) ^ (lane >> 3)) << 4);
-        }
       }
       // this wave's copies of tile i + 1 (issued one iteration ago) have landed
-      if (more) wait_vmcnt<ND>();
-      else wait_vmcnt<0>();
       __syncthreads();                                   // B_i
     }
     const float l_own = l_part + lane_xor16(l_part);
@@ -727,8 +687,23 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
     __syncthreads();                                     // B_end
   } else {
     // ------------------------------------------------------------ PV waves
-    __syncthreads();                                     // B_pre0
-    __syncthreads();                                     // B_pre1
+    // PV wave 4 + w copies row group w of every tile (lane l: slot l % 8 of
+    // row 8 w + l / 8); the scorers issue no copies.
+    __syncthreads();                                     // B_pre0: pairs 0-2 visible
+    auto gather_all = [&](int t) __attribute__((always_inline)) {
+      const unsigned char* src = gather_src(t);
+      const uint32_t dst = gather_dst(t);
+#pragma unroll
+      for (int cg = 0; cg < ND; ++cg) lds_dma16(src + cg * 128, dst + cg * (kRgW * 1024));
+    };
+    if (ntiles > 0) gather_all(0);
+    if (ntiles > 1) {
+      gather_all(1);
+      wait_vmcnt<ND>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();                                     // B_pre1: tile 0 landed
     const int d_base = w4 * 128;
     const int pv_Lt = ((n16 >> 1) & 1) ^ (((g & 1) << 2) | (n16 >> 2));
     const int pv_lane = (g >> 1) * 1024 + (((g & 1) << 2) + (n16 >> 2)) * 128 + 8 * (n16 & 1);
@@ -740,14 +715,6 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
       for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
     int idx_p = 0, page_p = -1;          // ring entries of tile i - 1, read one iteration ahead
     for (int i = 0; i <= ntiles; ++i) {
-      // wave 4 keeps the index ring going: in odd iterations the table
-      // entries of pair (i + 5) / 2 (first read in iteration i + 3) and the
-      // indices of pair (i + 7) / 2; waited for by the next iteration's end
-      const bool ring = wave == 4 && (i & 1) && ((i + 5) >> 1) * 2 < ntiles;
-      if (ring) {
-        issue_page((i + 5) >> 1);
-        issue_idx((i + 7) >> 1);
-      }
       const int om = (i & 1) * kTileW + (lane & 31);
       const int idx_c = sh.idx[(i >> 1) & 7][om];
       const int page_c = sh.page[(i >> 1) & 7][om];
@@ -800,7 +767,21 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
       }
       idx_p = idx_c;
       page_p = page_c;
-      if (ring) wait_vmcnt<2>();
+      // the copy of tile i + 2 (its table entries are visible since iteration
+      // i - 1), then -- wave 4, odd iterations -- the index ring: the table
+      // entries of pair (i + 5) / 2 and the indices of pair (i + 7) / 2.  What
+      // this iteration issued may stay in flight; tile i + 1 (issued one
+      // iteration ago) and older ring copies have landed before the barrier.
+      const bool more = i + 2 < ntiles;
+      if (more) gather_all(i + 2);
+      const bool ring = wave == 4 && (i & 1) && ((i + 5) >> 1) * 2 < ntiles;
+      if (ring) {
+        issue_page((i + 5) >> 1);
+        issue_idx((i + 7) >> 1);
+      }
+      if (more && ring) wait_vmcnt<ND + 2>();
+      else if (more) wait_vmcnt<ND>();
+      else if (ring) wait_vmcnt<2>();
       else wait_vmcnt<0>();
       __syncthreads();                                   // B_i
     }
