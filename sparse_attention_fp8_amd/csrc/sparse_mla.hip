@@ -474,18 +474,22 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 // over all tokens of a tile), waves 4-7 multiply (wave 4 + d: dims
 // 128 d .. 128 d + 127 of all four head tiles).  Tiles are 32 tokens in a
 // ring of four LDS buffers: in iteration i the scorers run QK and the softmax
-// of tile i while the PV waves accumulate tile i - 1 and then copy tile i + 2,
+// of tile i while the PV waves copy tile i + 2 and accumulate tile i - 1,
 // and one barrier ends the iteration.  Each SIMD holds one scoring and one PV
 // wave, so the softmax's VALU work overlaps the other wave's MFMAs; a
 // scorer holds all tokens of its head tile, so the tile maximum needs no
 // exchange; and each V^T read feeds four MFMAs.  Measured against the
-// eight-wave kernel above at 64 heads over 128 rows (k = 2048): 10.6 % fewer
-// cycles, of which 3.7 % come from the copies being issued by the PV waves
-// after their products (by the scorers inside or after the QK loop, or by the
-// PV waves before their products, it costs 2-6 %).  What bounds
-// it: the scorers' C-operand reads (each head tile reads the whole tile) run
-// at the LDS bandwidth, and the softmax and the LDS round trip of its stores
-// before the barrier follow them serially.
+// eight-wave kernel above at 64 heads over 128 rows (k = 2048): 15 % fewer
+// cycles.  The copies decide much of it: issued by the PV waves at the top of
+// the iteration, from table entries read an iteration ahead, they have almost
+// two iterations to land; issued after the PV products the kernel takes 4 %
+// more cycles, issued by the scorers 8-12 % more.  Every LDS read a wave
+// waits on after the barrier is issued in one batch (ring entries, rescale
+// flags, probabilities, first operands): each round trip there costs several
+// hundred cycles behind the scorers' operand reads.  What bounds it: the
+// scorers' QK (each head tile reads the whole tile; the PV products share the
+// matrix cores), then the softmax and its stores before the barrier, and on
+// the PV side the round trip of the probabilities and the products.
 constexpr int kTileW = 32;                            // tokens per tile
 constexpr int kRgW = kTileW / 8;                      // row groups per tile
 constexpr int kTileBytesW = kTileW * kChunks * 16;    // 36864
@@ -565,6 +569,16 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
     return row_src(t, 8 * w4 + (lane >> 3), v) + (((lane & 7) ^ (lane >> 3)) << 4);
   };
   auto gather_dst = [&](int t) -> uint32_t { return lds_addr(sh.tile[t & 3]) + w4 * 1024; };
+  // the same from ring entries read ahead (idx, page of this lane's row of tile t)
+  auto gather_src_pre = [&](int t, int idx, int page) -> const unsigned char* {
+    const int tok = 8 * w4 + (lane >> 3);
+    const bool valid = slot0 + t * kTileW + tok < slot1 && idx >= 0 && idx < e && page >= 0 &&
+                       page < a.batch.num_pages;
+    const unsigned char* row = valid ? reinterpret_cast<const unsigned char*>(a.kv + (int64_t)page * a.kv_stride +
+                                                                              (idx & 63) * kKvDim)
+                                     : reinterpret_cast<const unsigned char*>(g_zero_row);
+    return row + (((lane & 7) ^ (lane >> 3)) << 4);
+  };
 
   if (wave == 0 && ntiles > 0) {
 #pragma unroll
@@ -648,6 +662,15 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
         tmax = fmaxf(tmax, lane_xor32(tmax));
         float alpha;
         const bool rescale = lazy_max_advance(m_run, tmax, alpha);
+        {
+          // the next tile's mask before this tile's stores, so its wait on the
+          // ring reads (long landed) does not also wait for the stores
+          const int t = i + 1;
+          const bool v = t < ntiles && slot0 + t * kTileW + (lane & 31) < slot1 && idx_m >= 0 && idx_m < e &&
+                         page_m >= 0 && page_m < a.batch.num_pages;
+          mask_n = (uint32_t)__ballot(v);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         float psum = 0.f;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -668,12 +691,6 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
         if (g == 0) sh.alpha[sl][ht * 16 + n16] = alpha;
         const bool any = __ballot(rescale) != 0ull;
         if (lane == 0) sh.resc[sl][ht] = any ? 1 : 0;
-        {
-          const int t = i + 1;
-          const bool v = t < ntiles && slot0 + t * kTileW + (lane & 31) < slot1 && idx_m >= 0 && idx_m < e &&
-                         page_m >= 0 && page_m < a.batch.num_pages;
-          mask_n = (uint32_t)__ballot(v);
-        }
       }
       // this wave's copies of tile i + 1 (issued one iteration ago) have landed
       __syncthreads();                                   // B_i
@@ -704,6 +721,9 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
       wait_vmcnt<0>();
     }
     __syncthreads();                                     // B_pre1: tile 0 landed
+    // this lane's copy source entries of tile 2 (pair 1, visible since B_pre0)
+    int idx_g = sh.idx[1][8 * w4 + (lane >> 3)];
+    int page_g = sh.page[1][8 * w4 + (lane >> 3)];
     const int d_base = w4 * 128;
     const int pv_Lt = ((n16 >> 1) & 1) ^ (((g & 1) << 2) | (n16 >> 2));
     const int pv_lane = (g >> 1) * 1024 + (((g & 1) << 2) + (n16 >> 2)) * 128 + 8 * (n16 & 1);
@@ -718,7 +738,20 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
       const int om = (i & 1) * kTileW + (lane & 31);
       const int idx_c = sh.idx[(i >> 1) & 7][om];
       const int page_c = sh.page[(i >> 1) & 7][om];
+      // this lane's copy source of tile i + 3 (entries visible since iteration i)
+      const int og = ((i + 3) & 1) * kTileW + 8 * w4 + (lane >> 3);
+      const int idx_gn = sh.idx[((i + 3) >> 1) & 7][og];
+      const int page_gn = sh.page[((i + 3) >> 1) & 7][og];
       asm volatile("" ::: "memory");
+      // the copy of tile i + 2, into the buffer tile i - 2 left (its PV ended
+      // before the last barrier), from the entries read one iteration ago
+      const bool more = i + 2 < ntiles;
+      if (more) {
+        const unsigned char* src = gather_src_pre(i + 2, idx_g, page_g);
+        const uint32_t dst = gather_dst(i + 2);
+#pragma unroll
+        for (int cg = 0; cg < ND; ++cg) lds_dma16(src + cg * 128, dst + cg * (kRgW * 1024));
+      }
       if (i >= 1) {
         const int j = i - 1;
         const bool v = slot0 + j * kTileW + (lane & 31) < slot1 && idx_p >= 0 && idx_p < e && page_p >= 0 &&
@@ -726,14 +759,8 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
         const uint32_t mask = (uint32_t)__ballot(v);
         if (mask != 0u) {
           const int sl = j & 1;
-          if ((sh.resc[sl][0] | sh.resc[sl][1] | sh.resc[sl][2] | sh.resc[sl][3]) != 0) {
-#pragma unroll
-            for (int ht = 0; ht < 4; ++ht) {
-              const float al = sh.alpha[sl][ht * 16 + n16];
-#pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] *= al;
-            }
-          }
+          // one batch of reads: the rescale flags, the probabilities, the first V^T operands
+          const int4 rs = *reinterpret_cast<const int4*>(sh.resc[sl]);
           v8bf pb[4];
 #pragma unroll
           for (int ht = 0; ht < 4; ++ht) {
@@ -754,6 +781,14 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
           v8bf vr[kPvAheadW + 1];
 #pragma unroll
           for (int dt = 0; dt < kPvAheadW; ++dt) vr[dt] = v_operand(dt);
+          if ((rs.x | rs.y | rs.z | rs.w) != 0) {
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+              const float al = sh.alpha[sl][ht * 16 + n16];
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] *= al;
+            }
+          }
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
             if (dt + kPvAheadW < NDT) vr[(dt + kPvAheadW) % (kPvAheadW + 1)] = v_operand(dt + kPvAheadW);
@@ -767,18 +802,17 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
       }
       idx_p = idx_c;
       page_p = page_c;
-      // the copy of tile i + 2 (its table entries are visible since iteration
-      // i - 1), then -- wave 4, odd iterations -- the index ring: the table
-      // entries of pair (i + 5) / 2 and the indices of pair (i + 7) / 2.  What
-      // this iteration issued may stay in flight; tile i + 1 (issued one
-      // iteration ago) and older ring copies have landed before the barrier.
-      const bool more = i + 2 < ntiles;
-      if (more) gather_all(i + 2);
+      idx_g = idx_gn;
+      page_g = page_gn;
+      // wave 4, odd iterations: the index ring -- the table entries of pair
+      // (i + 5) / 2 and the indices of pair (i + 7) / 2
       const bool ring = wave == 4 && (i & 1) && ((i + 5) >> 1) * 2 < ntiles;
       if (ring) {
         issue_page((i + 5) >> 1);
         issue_idx((i + 7) >> 1);
       }
+      // landed before the barrier: tile i + 1 (issued one iteration ago) and
+      // the ring copies issued then; this iteration's may stay in flight
       if (more && ring) wait_vmcnt<ND + 2>();
       else if (more) wait_vmcnt<ND>();
       else if (ring) wait_vmcnt<2>();
