@@ -485,8 +485,9 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
 // two iterations to land; issued after the PV products the kernel takes 4 %
 // more cycles, issued by the scorers 8-12 % more.  Every LDS read a wave
 // waits on after the barrier is issued in one batch (ring entries, rescale
-// flags, probabilities, first operands): each round trip there costs several
-// hundred cycles behind the scorers' operand reads.  What bounds it: the
+// flags, probabilities), and the PV waves read their V^T operands for the
+// next iteration before it (2 % fewer cycles): each round trip after the
+// barrier costs several hundred cycles behind the scorers' operand reads.  What bounds it: the
 // scorers' QK (each head tile reads the whole tile; the PV products share the
 // matrix cores), then the softmax and its stores before the barrier, and on
 // the PV side the round trip of the probabilities and the products.
@@ -496,7 +497,6 @@ constexpr int kTileBytesW = kTileW * kChunks * 16;    // 36864
 constexpr int kBufW = 4;                              // tile buffers
 constexpr int kPairSlots = 8;                         // ring of 64-entry index / table slots
 constexpr int kQkAheadW = 4;                          // C-operand reads in flight in QK
-constexpr int kPvAheadW = 2;                          // V^T reads in flight in PV
 
 // Small arrays first: one per-lane base register plus 16-bit offsets reaches them.
 struct WsShared {
@@ -734,6 +734,23 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
     int idx_p = 0, page_p = -1;          // ring entries of tile i - 1, read one iteration ahead
+    // V^T operands (dims 16 dt .. 16 dt + 15 of this wave's 128, all 32 tokens) of tile t
+    auto v_operand = [&](int t, int dt) __attribute__((always_inline)) {
+      const unsigned char* vb = sh.tile[t & 3] + pv_part + pv_lane + (dt >> 2) * (kRgW * 1024) +
+                                ((pv_Lt ^ (2 * (dt & 3))) << 4);
+      const v4s lo = lds_read_tr16(vb);
+      const v4s hi = lds_read_tr16(vb + 2048);
+      const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      v8bf va;
+      __builtin_memcpy(&va, &vv, 16);
+      return va;
+    };
+    // V^T operands of tile i - 1, read before the last barrier: after it the
+    // scorers' operand reads fill the LDS queue, and a wave reading its
+    // operands there waits behind them
+    v8bf vpre[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vpre[dt] = v8bf{};
     for (int i = 0; i <= ntiles; ++i) {
       const int om = (i & 1) * kTileW + (lane & 31);
       const int idx_c = sh.idx[(i >> 1) & 7][om];
@@ -759,7 +776,7 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
         const uint32_t mask = (uint32_t)__ballot(v);
         if (mask != 0u) {
           const int sl = j & 1;
-          // one batch of reads: the rescale flags, the probabilities, the first V^T operands
+          // one batch of reads: the rescale flags and the probabilities
           const int4 rs = *reinterpret_cast<const int4*>(sh.resc[sl]);
           v8bf pb[4];
 #pragma unroll
@@ -768,19 +785,6 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
             const uint2 p1 = sh.p[sl][ht][1][g][n16];
             pb[ht] = as_v8bf(make_uint4(p0.x, p0.y, p1.x, p1.y));
           }
-          const unsigned char* pv_base = sh.tile[j & 3] + pv_part + pv_lane;
-          auto v_operand = [&](int dt) __attribute__((always_inline)) {
-            const unsigned char* vb = pv_base + (dt >> 2) * (kRgW * 1024) + ((pv_Lt ^ (2 * (dt & 3))) << 4);
-            const v4s lo = lds_read_tr16(vb);
-            const v4s hi = lds_read_tr16(vb + 2048);
-            const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            v8bf va;
-            __builtin_memcpy(&va, &vv, 16);
-            return va;
-          };
-          v8bf vr[kPvAheadW + 1];
-#pragma unroll
-          for (int dt = 0; dt < kPvAheadW; ++dt) vr[dt] = v_operand(dt);
           if ((rs.x | rs.y | rs.z | rs.w) != 0) {
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht) {
@@ -791,11 +795,9 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
           }
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            if (dt + kPvAheadW < NDT) vr[(dt + kPvAheadW) % (kPvAheadW + 1)] = v_operand(dt + kPvAheadW);
-            const v8bf va = vr[dt % (kPvAheadW + 1)];
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht)
-              acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[ht], acc[ht][dt], 0, 0, 0);
+              acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[dt], pb[ht], acc[ht][dt], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -804,6 +806,11 @@ __global__ void __launch_bounds__(512) sparse_mla_ws_kernel(MlaArgs a) {
       page_p = page_c;
       idx_g = idx_gn;
       page_g = page_gn;
+      // V^T operands of tile i (landed since the last barrier) for the next iteration
+      if (i < ntiles) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vpre[dt] = v_operand(i, dt);
+      }
       // wave 4, odd iterations: the index ring -- the table entries of pair
       // (i + 5) / 2 and the indices of pair (i + 7) / 2
       const bool ring = wave == 4 && (i & 1) && ((i + 5) >> 1) * 2 < ntiles;
