@@ -9,7 +9,12 @@
 // whole [64 heads x 64 tokens] block of one or two query rows with the fp8
 // MFMA v_mfma_f32_32x32x64_f8f6f4 (M = 32 heads, N = 32 tokens, K = 64; the
 // e4m3 decode happens inside the MFMA): 2 head tiles x 2 token steps x 2 K
-// halves = 8 instructions per row and page.  (The 16x16x128 shape needs
+// halves = 8 instructions per row and page, issued in pairs between the VALU
+// operations of the previous pair's epilogue (a software pipeline over
+// (row, token step, head tile) that holds two accumulators, not a row's
+// four: 3 % fewer cycles at two rows per page; the page's next copy then
+// waits longer to issue, since the CU's memory queue is what bounds the
+// steady state).  (The 16x16x128 shape needs
 // about 1.4x the issue time per product here, and that time was not hidden
 // behind the loads.)  C layout: lane l holds 16 heads of token l % 32, so the
 // weighted ReLU head sum is 32 in-lane FMAs (ReLU as one v_med3_f32) per
@@ -145,37 +150,26 @@ __device__ __forceinline__ void load_qrow(QRow& t, const uint8_t* q, const float
   }
 }
 
-// sum_h w_h * relu(q_h . k_s) for token `lane` of the page (before the K
-// scale).  b[ks][kh]: B operand of token step ks (32 tokens), K half kh.
-__device__ __forceinline__ float page_row_logit(const QRow& qr, const v8i (&b)[2][2]) {
-  // all eight products are issued before the first epilogue reads one
+// A half unit: one query row, one token step (32 tokens), one head tile
+// (32 heads): the MFMA pair over both K halves.  b[kh]: B operand of the step.
+__device__ __forceinline__ void half_mfma(const QRow& qr, const v8i (&b)[2], int mt, v16f& acc) {
   const v16f z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  v16f acc[2][2];
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qr.q[mt][0], b[0], z, 0, 0, 0, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qr.q[mt][1], b[1], acc, 0, 0, 0, 0, 0, 0);
+}
+
+// Its weighted ReLU terms added into the four partial sums p (head tile 0
+// first, then head tile 1, so the sum's order is fixed).
+__device__ __forceinline__ void half_epilogue(const QRow& qr, int mt, const v16f& acc, float (&p)[4]) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      acc[ks][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qr.q[mt][0], b[ks][0], z, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      acc[ks][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qr.q[mt][1], b[ks][1], acc[ks][mt],
-                                                                    0, 0, 0, 0, 0, 0);
-  float part[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    float p[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i & 3] = fmaf(qr.w[mt][i], relu_finite(acc[ks][mt][i]), p[i & 3]);
-    part[ks] = (p[0] + p[1]) + (p[2] + p[3]);
-  }
-  // Lane l holds half the heads of token l % 32 of both steps; one lane swap
-  // gives lanes 0-31 the other half of step 0 and lanes 32-63 the other half
-  // of step 1, so afterwards lane l holds page token l.
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+  for (int i = 0; i < 16; ++i) p[i & 3] = fmaf(qr.w[mt][i], relu_finite(acc[i]), p[i & 3]);
+}
+
+// Lane l holds half the heads of token l % 32 of both steps; one lane swap
+// gives lanes 0-31 the other half of step 0 and lanes 32-63 the other half
+// of step 1, so afterwards lane l holds page token l.
+__device__ __forceinline__ float row_logit(float part0, float part1) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part0), __float_as_uint(part1), false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
@@ -321,13 +315,52 @@ __global__ void __launch_bounds__(64 * kWavesPg) indexer_paged_kernel(PagedArgs 
         for (int jj = 0; jj < QL; ++jj)
           if (g0 + jj < nrows) load_qrow(qr[jj], a.q, a.w, row0 + g0 + jj, lane);
       }
+      // Software pipeline over half units h = (row jj, step ks, head tile
+      // mt), in that order: the MFMA pair of half unit h + 1 is issued
+      // between the VALU operations of half unit h's epilogue.  A group with
+      // fewer than QL rows runs every half unit anyway (the extra rows'
+      // results are dropped), so the schedule has no branches.
+      constexpr int NH = 4 * QL;
+      v16f acc[2];
+      float p[QL][2][4];
+#pragma unroll
+      for (int jj = 0; jj < QL; ++jj)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) p[jj][ks][c] = 0.f;
+      half_mfma(qr[0], bop[0], 0, acc[0]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int hn = h + 1;
+        if (hn < NH) half_mfma(qr[hn >> 2], bop[(hn >> 1) & 1], hn & 1, acc[hn & 1]);
+        half_epilogue(qr[h >> 2], h & 1, acc[h & 1], p[h >> 2][(h >> 1) & 1]);
+        if (hn < NH) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float part[QL][2];
+#pragma unroll
+      for (int jj = 0; jj < QL; ++jj)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          part[jj][ks] = (p[jj][ks][0] + p[jj][ks][1]) + (p[jj][ks][2] + p[jj][ks][3]);
+          // computed here, not sunk into the store's branch below
+          asm volatile("" : "+v"(part[jj][ks]));
+        }
 #pragma unroll
       for (int jj = 0; jj < QL; ++jj) {
         if (g0 + jj >= nrows) break;
         const int r = row0 + g0 + jj;
         int e = L - q_len + (r - q0) + 1;
         e = e < 0 ? 0 : e;
-        const float v = id >= 0 ? page_row_logit(qr[jj], bop) * scale : -INFINITY;
+        const float v = id >= 0 ? row_logit(part[jj][0], part[jj][1]) * scale : -INFINITY;
         float* dst = a.logits + (int64_t)r * a.logits_stride + s;
         if (s < e) {
           if (in_stride) *dst = v;
