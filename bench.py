@@ -420,10 +420,69 @@ def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True
                                  "hbm_frac": nbytes[other_mla] / (alt_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                  "note": "the same indices through the other latent-cache format"}
         res["pre_path"] = pre_path(dsa, wl, batch, base, dev, args.steps)
+        if not prefill:
+            res["page_read"] = page_read_ceiling(wl, [t["idx_cache"] for t in sets], dev, reps)
         res["wl"] = wl
     del sets, base
     torch.cuda.synchronize()
     return res
+
+
+def page_read_ceiling(wl, caches, dev, reps):
+    """Rate at which this GPU reads the indexer's pages with the indexer's copy
+    scheme and no arithmetic: the probe library reads every page the paged
+    indexer reads (same page list, order and launch shape), rotating over the
+    same cache copies.  Returns None when the probe library is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_attention_fp8_amd", "libdsa_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.dsa_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.dsa_probe_page_read.restype = ctypes.c_int
+    bt, sl, qs = wl.block_table.numpy(), wl.seq_lens.numpy(), wl.query_start.numpy()
+    ids = []
+    for b in range(len(sl)):
+        if qs[b + 1] > qs[b]:
+            n = (min(int(sl[b]), wl.max_seq_len) + 63) // 64
+            ids.extend(int(x) for x in bt[b, :n])
+    ids_dev = torch.tensor(ids, dtype=torch.int32, device=dev)
+    assert len(ids) == 0 or (0 <= int(ids_dev.min()) and int(ids_dev.max()) < wl.num_pages)
+    max_pages = len(sl) * ((wl.max_seq_len + 63) // 64)
+    grid = max(1, min(torch.cuda.get_device_properties(0).multi_processor_count, (max_pages + 7) // 8))
+    out = torch.empty(grid * 512, dtype=torch.int32, device=dev)
+    page_bytes = 64 * 132
+    stride = caches[0].stride(0) * caches[0].element_size()
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        # the stream current at the call: under capture that is the capturing stream
+        rc = lib.dsa_probe_page_read(ctypes.c_void_p(caches[i % len(caches)].data_ptr()), stride,
+                                     ctypes.c_void_p(ids_dev.data_ptr()), len(ids), ctypes.c_void_p(out.data_ptr()),
+                                     grid, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == 0, f"page-read probe launch failed ({rc})"
+
+    launch(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rounds = 4
+    e0.record(stream)
+    for _ in range(rounds):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (rounds * reps)
+    nbytes = len(ids) * page_bytes
+    return {"us": ms * 1e3, "GBps": nbytes / (ms * 1e-3) / 1e9, "pages": len(ids), "bytes": nbytes,
+            "grid": grid, "note": "the paged indexer's pages read with its copy scheme and launch shape, "
+                                  "no arithmetic (probe/page_read.hip)"}
 
 
 def copy_rate_gbs():
@@ -483,6 +542,10 @@ def main():
         "other_kv_stage": head["other_kv_stage"],
         "pre_path": head["pre_path"],
     }
+    if head.get("page_read"):
+        pr = head["page_read"]
+        pr["indexer_stage_over_page_read"] = head["stage_ms"]["indexer"] * 1e3 / pr["us"]
+        line["page_read"] = pr
     wl = head.pop("wl")
     del head
     # the other decode workloads, measured in the same run (same timing method)

@@ -1,7 +1,8 @@
 """Build libdsa.so in-tree with hipcc for gfx950 (no runtime compilation).
 
 Every HIP source is compiled to an object under ``_build/`` (in parallel) and
-linked into ``sparse_attention_fp8_amd/libdsa.so``.  Packed-fp32 instruction
+linked into ``sparse_attention_fp8_amd/libdsa.so``; the page-read ceiling probe
+that bench.py runs is built beside it as ``libdsa_probe.so``.  Packed-fp32 instruction
 selection is switched off for all device code.
 """
 from __future__ import annotations
@@ -19,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
+# the read-only ceiling probe bench.py runs next to the step (not part of libdsa)
+PROBE_SRC = os.path.join(PKG, "probe", "page_read.hip")
+PROBE_LIB = os.path.join(PKG, "libdsa_probe.so")
 ARCH = "gfx950"
 
 
@@ -58,7 +62,19 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+def build_probe() -> str:
+    """Compile the page-read ceiling probe into libdsa_probe.so."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), "-x", "hip", "-shared", PROBE_SRC, "-o", tmp] + common_flags()
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
