@@ -22,6 +22,9 @@
 //    accumulates separately, so z = sum_g scale_g * acc_g + acc_rope in fp32
 //    keeps every product exact.  One 128-bit read feeds two MFMAs (the k
 //    order inside a 64-dim pair is permuted identically for C and q).
+//  * 64-head blocks use the wave-specialised kernel at the end of this file
+//    (codes converted once per tile into a bf16 tile, scorers and PV waves
+//    on each SIMD); the notes below are the 16- and 32-head forms'.
 //  * PV: the V^T operand is read with the 8-bit transposing LDS read
 //    (ds_read_b64_tr_b8: lane n gets byte n % 8 of the vectors of lanes
 //    n / 8 + 2 j) and converted to bf16 exactly; the group scale is folded
@@ -458,6 +461,437 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// 64-head blocks over the fp8 cache, wave-specialised like the bf16 kernel's
+// 64-head form: waves 0-3 score (wave w: head tile w over all 32 tokens of a
+// tile), waves 4-7 multiply (wave 4 + w: dims 128 w .. 128 w + 127, which is
+// exactly scale group w, of all four head tiles).  PV wave 4 + w copies row
+// group w (8 tokens: 640 bytes of codes and rope, 16 bytes of scales) of each
+// tile into a ring of three fp8 buffers three tiles ahead, and one iteration
+// before a tile is scored it converts those rows (e4m3 -> bf16, exact, scale
+// 1) into one of two bf16 tiles laid out as the bf16 kernel's, rope copied.
+// The scorers then run the bf16 kernel's QK with one accumulator per scale
+// group (and one for the rope): z = rope + sum_g scale_g * acc_g in fp32
+// keeps every product exact.  The scorers store fp32 probabilities; PV wave
+// 4 + w folds its own group's scale in, P'_w = bf16(p * scale_w), and
+// multiplies the converted V^T.  The index ring is kept by scorer wave 0, so
+// the PV waves' memory counters hold only their copies.  At 64 heads over
+// 128 rows (k = 2048) it takes 7.7 % fewer cycles than the four-head-tile
+// form of the kernel above; the PV waves bound it (probability scaling,
+// conversion and copies on top of the products: ~3,800 cycles an iteration
+// against the scorers' ~2,100).
+constexpr int kTileF = 32;                               // tokens per tile
+constexpr int kRgF = kTileF / 8;                         // row groups per tile
+constexpr int kCvBytes = kTileF * kKvDim * 2;            // 36864: converted tile (bf16 layout)
+constexpr int kF8Scale = 5 * kRgF * 1024;                // 20480: scale records in an fp8 ring tile
+constexpr int kF8Bytes = kF8Scale + kTileF * 16;         // 20992
+constexpr int kF8Buf = 3;                                // fp8 ring tiles
+constexpr int kPairSlotsF = 8;
+constexpr int kQkAheadF = 4;
+constexpr int kCopiesF = 6;                              // copies per PV wave and tile (5 column groups + scales)
+
+struct WsShared8 {
+  float4 pf[2][4][2][4][16];        // fp32 probabilities [tile & 1][head tile][token tile][g][head]
+  float alpha[2][64];               // rescale factor of each head for tile & 1
+  int resc[2][4];                   // scorer w moved the reference max of some head in tile & 1
+  float m[64];                      // final reference max of each head (log2 domain)
+  float l[64];                      // final row sum of each head
+  int idx[kPairSlotsF][64];         // indices of tiles 2P, 2P + 1 in slot P % 8
+  int page[kPairSlotsF][64];        // their block-table entries
+  float4 scl[3][kTileF];            // the 4 group scales of each token of tile t in slot t % 3
+  unsigned char cv[2][kCvBytes];    // converted tiles (bf16, the bf16 kernel's tile layout)
+  unsigned char f8[kF8Buf][kF8Bytes];   // copied fp8 rows: 1 KB blocks (column group, row group), unswizzled
+};
+
+__global__ void __launch_bounds__(512) sparse_mla_fp8_ws_kernel(MlaArgs a) {
+  constexpr int NDT = 8;                  // 16-dim tiles per PV wave
+  __shared__ WsShared8 sh;
+
+  const int R = a.batch.num_rows;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n16 = lane & 15;
+  const int bid = blockIdx.x;
+  const int q8 = bid >> 3;
+  const int hb = q8 % a.head_blocks;
+  const int rest = (q8 / a.head_blocks) * 8 + (bid & 7);
+  if (rest >= R * a.splits) return;
+  const int r = rest / a.splits;
+  const int sp = rest % a.splits;
+  const int hbase = hb * 64;
+  const bool scorer = wave < 4;
+  const int w4 = wave & 3;
+
+  const int slot0 = sp * a.split_slots;
+  const int slot1 = min(slot0 + a.split_slots, a.k);
+  const int ntiles = (slot1 - slot0 + kTileF - 1) / kTileF;
+
+  // Index ring: the indices of tile pair P go to slot P % 8 of sh.idx, then
+  // their block-table entries to sh.page (wave 0: pairs 0-4 and 0-3 before
+  // the loop, pair (i + 9) / 2 and (i + 7) / 2 after odd iterations i).
+  const int32_t* idx_row = a.indices + (int64_t)r * a.k;
+  int bc = 0, e = 0;
+  auto issue_idx = [&](int P) {
+    const int j = min(slot0 + P * 64 + lane, slot1 - 1);
+    lds_dma4(idx_row + j, lds_addr(sh.idx[P & 7]));
+  };
+  auto issue_page_from = [&](int P, int idx) {
+    const int ic = (idx >= 0 && idx < a.batch.max_seq_len) ? idx : 0;
+    lds_dma4(a.batch.block_table + (int64_t)bc * a.batch.bt_stride + (ic >> 6), lds_addr(sh.page[P & 7]));
+  };
+  auto entry = [&](int t, int tok, int& ix, int& pg) __attribute__((always_inline)) {
+    const int o = (t & 1) * kTileF + tok;
+    ix = sh.idx[(t >> 1) & 7][o];
+    pg = sh.page[(t >> 1) & 7][o];
+  };
+  auto valid_tok = [&](int t, int tok, int ix, int pg) __attribute__((always_inline)) {
+    return slot0 + t * kTileF + tok < slot1 && ix >= 0 && ix < e && pg >= 0 && pg < a.batch.num_pages;
+  };
+
+  if (wave == 0 && ntiles > 0) {
+#pragma unroll
+    for (int P = 0; P < 5; ++P) issue_idx(P);
+  }
+  {
+    int b;
+    seq_and_extent_wave(a.batch, r, b, e);
+    bc = b >= 0 ? b : 0;
+  }
+
+  if (scorer) {
+    // ------------------------------------------------------------ scorers
+    const int ht = w4;
+    const int hq = hbase + ht * 16 < a.H ? hbase + ht * 16 + n16 : hbase + n16;
+    uint4 qreg[18];
+    {
+      const uint16_t* qp = a.q + ((int64_t)r * a.H + hq) * kKvDim + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+    }
+    wait_vmcnt<0>();
+    if (wave == 0 && ntiles > 0) {
+#pragma unroll
+      for (int P = 0; P < 4; ++P) issue_page_from(P, sh.idx[P & 7][lane]);
+      wait_vmcnt<0>();
+    }
+    __syncthreads();                                     // B_pre0: table entries of pairs 0-3 visible
+    __syncthreads();                                     // B_pre1: tile 0 converted
+
+    const int r8 = n16 & 7;
+    const int qk0 = (n16 >> 3) * 1024 + r8 * 128 + ((g ^ r8) << 4);
+    float m_run = kMaskSentinel;
+    float l_part = 0.f;
+    uint32_t mask_n = 0u;
+    if (ntiles > 0) {
+      int ix, pg;
+      entry(0, lane & 31, ix, pg);
+      mask_n = (uint32_t)__ballot(valid_tok(0, lane & 31, ix, pg));
+    }
+    for (int i = 0; i <= ntiles; ++i) {
+      const bool ring = wave == 0 && (i & 1) && ((i + 7) >> 1) * 2 < ntiles;
+      if (i < ntiles) {
+        const uint32_t mask = mask_n;
+        // ring entries for the next mask, the tile's scales, wave 0's index for its table lookups
+        int idx_m, page_m;
+        entry(i + 1, lane & 31, idx_m, page_m);
+        const int idx_r = sh.idx[((i + 7) >> 1) & 7][lane];
+        float4 sc[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[tt][j] = sh.scl[i % 3][16 * tt + 4 * g + j];
+        asm volatile("" ::: "memory");   // issue those reads here, ahead of the QK operand reads
+        const int sl = i & 1;
+        // accumulators: scale groups 0-3 of the latent dims, then the rope
+        v4f s[5][2];
+#pragma unroll
+        for (int gg = 0; gg < 5; ++gg)
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) s[gg][tt] = v4f{0.f, 0.f, 0.f, 0.f};
+        if (mask != 0u) {
+          const unsigned char* tile = sh.cv[i & 1];
+          // step q: token tile q & 1, k-step q >> 1 (scale group (q >> 1) / 4, rope from k-step 16)
+          auto c_operand = [&](int q) __attribute__((always_inline)) {
+            const int tt = q & 1, ks = q >> 1;
+            return *reinterpret_cast<const uint4*>(tile + (qk0 ^ ((ks & 1) << 6)) + (ks >> 1) * (kRgF * 1024) +
+                                                   tt * 2048);
+          };
+          uint4 cr[kQkAheadF + 1];
+#pragma unroll
+          for (int q = 0; q < kQkAheadF; ++q) cr[q] = c_operand(q);
+#pragma unroll
+          for (int q = 0; q < 36; ++q) {
+            if (q + kQkAheadF < 36) cr[(q + kQkAheadF) % (kQkAheadF + 1)] = c_operand(q + kQkAheadF);
+            const int gg = (q >> 1) < 16 ? (q >> 3) : 4;
+            s[gg][q & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_v8bf(cr[q % (kQkAheadF + 1)]),
+                                                                  as_v8bf(qreg[q >> 1]), s[gg][q & 1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        // softmax of head tile ht over the tile's 32 tokens (token 16 tt + 4 g + j in s[.][tt][j])
+        float z[2][4];
+        float tmax = kMaskSentinel;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float d = s[4][tt][j];
+            d = fmaf(sc[tt][j].x, s[0][tt][j], d);
+            d = fmaf(sc[tt][j].y, s[1][tt][j], d);
+            d = fmaf(sc[tt][j].z, s[2][tt][j], d);
+            d = fmaf(sc[tt][j].w, s[3][tt][j], d);
+            const bool v = (mask >> (16 * tt + 4 * g + j)) & 1u;
+            z[tt][j] = v ? d * a.scale_log2 : kMaskSentinel;
+            tmax = fmaxf(tmax, z[tt][j]);
+          }
+        tmax = fmaxf(tmax, lane_xor16(tmax));
+        tmax = fmaxf(tmax, lane_xor32(tmax));
+        float alpha;
+        const bool rescale = lazy_max_advance(m_run, tmax, alpha);
+        {
+          const int t = i + 1;
+          const bool v = t < ntiles && valid_tok(t, lane & 31, idx_m, page_m);
+          mask_n = (uint32_t)__ballot(v);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float psum = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          float pv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool v = (mask >> (16 * tt + 4 * g + j)) & 1u;
+            pv[j] = v ? __builtin_amdgcn_exp2f(z[tt][j] - m_run) : 0.f;
+            psum += pv[j];
+          }
+          sh.pf[sl][ht][tt][g][n16] = make_float4(pv[0], pv[1], pv[2], pv[3]);
+        }
+        l_part = l_part * alpha + psum;
+        if (g == 0) sh.alpha[sl][ht * 16 + n16] = alpha;
+        const bool any = __ballot(rescale) != 0ull;
+        if (lane == 0) sh.resc[sl][ht] = any ? 1 : 0;
+        // wave 0, odd iterations: the index ring -- table entries of pair
+        // (i + 7) / 2, indices of pair (i + 9) / 2; they land before the next barrier
+        if (ring) {
+          issue_page_from((i + 7) >> 1, idx_r);
+          issue_idx((i + 9) >> 1);
+        }
+      }
+      if (ring) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+      __syncthreads();                                   // B_i
+    }
+    const float l_own = l_part + lane_xor16(l_part);
+    const float l_sum = l_own + lane_xor32(l_own);
+    if (g == 0) {
+      sh.m[ht * 16 + n16] = m_run;
+      sh.l[ht * 16 + n16] = l_sum;
+    }
+    __syncthreads();                                     // B_end
+  } else {
+    // ------------------------------------------------------------ PV waves
+    // Copy of tile t (row group w4 into fp8 buffer t % 3): lane l copies slot
+    // l & 7 of row l / 8 of each 128-byte column group (4 of codes, 1 of
+    // rope); lanes 0-7 copy the scale records of the group's 8 tokens.
+    auto copy_fp8 = [&](int t, int ix, int pg, int ixs, int pgs) __attribute__((always_inline)) {
+      const int tok = 8 * w4 + (lane >> 3);
+      const unsigned char* row =
+          valid_tok(t, tok, ix, pg) ? a.kv8 + (int64_t)pg * a.kv8_stride + (ix & 63) * kRow8
+                                    : reinterpret_cast<const unsigned char*>(g_zero_row8);
+      const uint32_t dst = lds_addr(sh.f8[t % kF8Buf]);
+#pragma unroll
+      for (int cg = 0; cg < 5; ++cg) lds_dma16(row + cg * 128 + ((lane & 7) << 4), dst + (cg * kRgF + w4) * 1024);
+      const int toks = 8 * w4 + (lane & 7);
+      const unsigned char* srec =
+          valid_tok(t, toks, ixs, pgs) ? a.kv8 + (int64_t)pgs * a.kv8_stride + kScaleOff8 + (ixs & 63) * 16
+                                       : reinterpret_cast<const unsigned char*>(g_zero_row8);
+      if (lane < 8) lds_dma16(srec, dst + kF8Scale + w4 * 128);
+    };
+    // Conversion of tile t's row group w4: lane l takes row l / 8, 16-byte
+    // slot l & 7 of each column group; codes go to the bf16 tile (slot s of
+    // row r8 holds chunk s ^ r8, as the bf16 kernel's copies leave it), rope
+    // is copied, lanes 0-7 move the scale records.
+    auto convert = [&](int t) __attribute__((always_inline)) {
+      const unsigned char* src = sh.f8[t % kF8Buf];
+      unsigned char* dst = sh.cv[t & 1];
+      const int r8 = lane >> 3, c = lane & 7;
+      uint4 raw[5];
+#pragma unroll
+      for (int cg = 0; cg < 5; ++cg)
+        raw[cg] = *reinterpret_cast<const uint4*>(src + (cg * kRgF + w4) * 1024 + lane * 16);
+      float4 srec = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (lane < 8) srec = *reinterpret_cast<const float4*>(src + kF8Scale + (8 * w4 + lane) * 16);
+#pragma unroll
+      for (int cg8 = 0; cg8 < 4; ++cg8) {
+        // 16 codes: dims 128 cg8 + 16 c .. + 15 -> bf16 column group 2 cg8 + c / 4, chunks 2 (c % 4) and + 1
+        const uint4 w = raw[cg8];
+        const uint4 lo = make_uint4(fp8x2_to_bf16x2(w.x, false), fp8x2_to_bf16x2(w.x, true),
+                                    fp8x2_to_bf16x2(w.y, false), fp8x2_to_bf16x2(w.y, true));
+        const uint4 hi = make_uint4(fp8x2_to_bf16x2(w.z, false), fp8x2_to_bf16x2(w.z, true),
+                                    fp8x2_to_bf16x2(w.w, false), fp8x2_to_bf16x2(w.w, true));
+        const int cg = 2 * cg8 + (c >> 2), ch = 2 * (c & 3);
+        unsigned char* blk = dst + (cg * kRgF + w4) * 1024 + r8 * 128;
+        *reinterpret_cast<uint4*>(blk + ((ch ^ r8) << 4)) = lo;
+        *reinterpret_cast<uint4*>(blk + (((ch + 1) ^ r8) << 4)) = hi;
+      }
+      *reinterpret_cast<uint4*>(dst + (8 * kRgF + w4) * 1024 + r8 * 128 + ((c ^ r8) << 4)) = raw[4];
+      if (lane < 8) sh.scl[t % 3][8 * w4 + lane] = srec;
+    };
+    __syncthreads();                                     // B_pre0: table entries of pairs 0-3 visible
+    int ixg = 0, pgg = 0, ixs = 0, pgs = 0;              // entries of this lane's rows of the next tile to copy
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      if (t < ntiles) {
+        entry(t, 8 * w4 + (lane >> 3), ixg, pgg);
+        entry(t, 8 * w4 + (lane & 7), ixs, pgs);
+        copy_fp8(t, ixg, pgg, ixs, pgs);
+      }
+    }
+    entry(3, 8 * w4 + (lane >> 3), ixg, pgg);
+    entry(3, 8 * w4 + (lane & 7), ixs, pgs);
+    if (ntiles > 0) {
+      if (ntiles > 2) wait_vmcnt<2 * kCopiesF>();
+      else if (ntiles > 1) wait_vmcnt<kCopiesF>();
+      else wait_vmcnt<0>();
+      convert(0);
+    }
+    __syncthreads();                                     // B_pre1: tile 0 converted
+    const int d_base = w4 * 128;
+    const int pv_Lt = ((n16 >> 1) & 1) ^ (((g & 1) << 2) | (n16 >> 2));
+    const int pv_lane = (g >> 1) * 1024 + (((g & 1) << 2) + (n16 >> 2)) * 128 + 8 * (n16 & 1);
+    const int pv_part = (d_base >> 6) * (kRgF * 1024);
+    v4f acc[4][NDT];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    int idx_p = 0, page_p = -1;          // ring entries of tile i - 1, read one iteration ahead
+    // V^T operands (dims 16 dt .. 16 dt + 15 of this wave's 128, all 32 tokens) of converted tile t
+    auto v_operand = [&](int t, int dt) __attribute__((always_inline)) {
+      const unsigned char* vb = sh.cv[t & 1] + pv_part + pv_lane + (dt >> 2) * (kRgF * 1024) +
+                                ((pv_Lt ^ (2 * (dt & 3))) << 4);
+      const v4s lo = lds_read_tr16(vb);
+      const v4s hi = lds_read_tr16(vb + 2048);
+      const v8s vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      v8bf va;
+      __builtin_memcpy(&va, &vv, 16);
+      return va;
+    };
+    v8bf vpre[NDT];                      // V^T operands of tile i - 1, read before the last barrier
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vpre[dt] = v8bf{};
+    for (int i = 0; i <= ntiles; ++i) {
+      int idx_c, page_c;
+      entry(i, lane & 31, idx_c, page_c);
+      // this wave's row group of tile i + 3 into the fp8 buffer tile i left
+      // (converted last iteration); entries read one iteration ago
+      const bool more3 = i + 3 < ntiles;
+      if (more3) copy_fp8(i + 3, ixg, pgg, ixs, pgs);
+      entry(i + 4, 8 * w4 + (lane >> 3), ixg, pgg);
+      entry(i + 4, 8 * w4 + (lane & 7), ixs, pgs);
+      asm volatile("" ::: "memory");
+      if (i >= 1) {
+        const int j = i - 1;
+        const bool v = valid_tok(j, lane & 31, idx_p, page_p);
+        const uint32_t mask = (uint32_t)__ballot(v);
+        if (mask != 0u) {
+          const int sl = j & 1;
+          // one batch of reads: the rescale flags, the probabilities, this group's scales
+          const int4 rs = *reinterpret_cast<const int4*>(sh.resc[sl]);
+          float4 pp[4][2];
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) pp[ht][tt] = sh.pf[sl][ht][tt][g][n16];
+          float sw[2][4];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              sw[tt][jj] = reinterpret_cast<const float*>(&sh.scl[j % 3][16 * tt + 4 * g + jj])[w4];
+          v8bf pb[4];
+#pragma unroll
+          for (int ht = 0; ht < 4; ++ht) {
+            uint4 u;
+            u.x = pack_bf16x2(pp[ht][0].x * sw[0][0], pp[ht][0].y * sw[0][1]);
+            u.y = pack_bf16x2(pp[ht][0].z * sw[0][2], pp[ht][0].w * sw[0][3]);
+            u.z = pack_bf16x2(pp[ht][1].x * sw[1][0], pp[ht][1].y * sw[1][1]);
+            u.w = pack_bf16x2(pp[ht][1].z * sw[1][2], pp[ht][1].w * sw[1][3]);
+            pb[ht] = as_v8bf(u);
+          }
+          if ((rs.x | rs.y | rs.z | rs.w) != 0) {
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+              const float al = sh.alpha[sl][ht * 16 + n16];
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) acc[ht][dt] *= al;
+            }
+          }
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht)
+              acc[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vpre[dt], pb[ht], acc[ht][dt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      idx_p = idx_c;
+      page_p = page_c;
+      // tile i + 1: its copies (issued two iterations ago) have landed once at
+      // most the later tiles' copies are in flight; converted for the next iteration
+      if (i + 1 < ntiles) {
+        const bool more2 = i + 2 < ntiles;
+        if (more2 && more3) wait_vmcnt<2 * kCopiesF>();
+        else if (more2 | more3) wait_vmcnt<kCopiesF>();
+        else wait_vmcnt<0>();
+        convert(i + 1);
+      }
+      // V^T operands of tile i for the next iteration
+      if (i < ntiles) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vpre[dt] = v_operand(i, dt);
+      }
+      __syncthreads();                                   // B_i
+    }
+    __syncthreads();                                     // B_end: m and l of every head
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+      if (hbase + ht * 16 >= a.H) continue;              // a missing head tile
+      const int hp = hbase + ht * 16 + n16;
+      const float l_tot = sh.l[ht * 16 + n16];
+      const float m_fin = sh.m[ht * 16 + n16];
+      if (a.splits == 1) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* op = a.out + ((int64_t)r * a.H + hp) * kVDim + d_base + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const v4f o = acc[ht][dt];
+          uint2 pk;
+          pk.x = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
+          pk.y = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
+          *reinterpret_cast<uint2*>(op + dt * 16) = pk;
+        }
+        if (w4 == 0 && g == 0)
+          a.lse[(int64_t)r * a.H + hp] = l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t base = ((int64_t)sp * R + r) * a.H + hp;
+        float* pa = a.part_acc + base * kVDim + d_base + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const v4f o = acc[ht][dt];
+          *reinterpret_cast<float4*>(pa + dt * 16) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+        if (w4 == 0 && g == 0) {
+          a.part_ml[base * 2] = l_tot > 0.f ? m_fin : kMaskSentinel;
+          a.part_ml[base * 2 + 1] = l_tot;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_sparse_mla_fp8(const BatchArgs& batch, const uint16_t* q, int H, const uint8_t* kv8,
@@ -492,7 +926,7 @@ hipError_t launch_sparse_mla_fp8(const BatchArgs& batch, const uint16_t* q, int 
   } else if (H == 32) {
     hipLaunchKernelGGL((sparse_mla_fp8_kernel<2, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((sparse_mla_fp8_kernel<4, 2>), dim3((unsigned)grid), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(sparse_mla_fp8_ws_kernel, dim3((unsigned)grid), dim3(512), 0, stream, a);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.splits <= 1) return err;
