@@ -371,7 +371,8 @@ __global__ void __launch_bounds__(64 * kWavesPg) indexer_paged_kernel(PagedArgs 
     }
     // page p + kRingPg goes into this slot (its data is in registers since
     // the wait above); issued after the page's products and stores rather
-    // than before them (GRBM cycles c5 -0.9 %, c2 -4.2 %)
+    // than before them (GRBM cycles -0.9 % with two query rows per page over
+    // 64 sequences, -4.2 % with one row per page over 32 sequences)
     if (p + kRingPg < p_end) issue(p + kRingPg);
   };
 

@@ -26,8 +26,8 @@
 //    from HBM straight into LDS with global_load_lds_dwordx4 into two buffers.
 //    With 16 heads the copy of tile i+2 is issued as soon as tile i's buffer
 //    is released, so two tiles are in flight whenever a wave waits (a wait
-//    with one tile in flight leaves the HBM queue half empty: a c2-sized
-//    gather takes about 1.6x as long).  Larger head blocks keep one tile
+//    with one tile in flight leaves the HBM queue half empty: the gather of
+//    32 decode rows of 16 heads over k = 2048 takes about 1.6x as long).  Larger head blocks keep one tile
 //    ahead and spread its copy over the QK steps of the tile being
 //    multiplied, which hides the copy issue behind their MFMAs.  Each lane
 //    supplies its own source address, so the gather through the block table

@@ -232,8 +232,8 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_fp8_kernel(MlaArgs a)
     for (int i = 0; i < ND; ++i) gather_one(src, ssrc, dst, i);
   };
   // Two tiles in flight pay off only once the pipeline runs for a while: with
-  // 4 tiles per split (c2) asking for two at once delays the first (24.9 us
-  // against 24.0 us).
+  // 4 tiles per split (32 decode rows of 16 heads, 8 splits) asking for two
+  // at once delays the first (24.9 us against 24.0 us).
   const int depth = (DEPTH > 1 && ntiles >= kDeepTiles) ? DEPTH : 1;
   // q went out before the prologue's loads and the prologue waited for those,
   // so inside the loop no load but the copies is ever outstanding and the
