@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(256) sparse_mla_merge_kernel(MlaArgs a) {
   uint32_t pk[DPL / 2];
 #pragma unroll
   for (int d = 0; d < DPL / 2; ++d)
-    pk[d] = (uint32_t)f32_to_bf16_rne(o[2 * d] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * d + 1] * inv) << 16);
+    pk[d] = pack_bf16x2(o[2 * d] * inv, o[2 * d + 1] * inv);
   uint16_t* dst = a.out + pair * kVDim + d0;
   if constexpr (DPL == 8) *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   else if constexpr (DPL == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);

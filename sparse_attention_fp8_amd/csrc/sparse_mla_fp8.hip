@@ -856,26 +856,47 @@ __global__ void __launch_bounds__(512) sparse_mla_fp8_ws_kernel(MlaArgs a) {
       __syncthreads();                                   // B_i
     }
     __syncthreads();                                     // B_end: m and l of every head
+    if (a.splits == 1) {
+      // This wave's output (64 heads x its 128 dims) is staged as bf16 rows of
+      // 256 B in half a converted-tile buffer (free: no copy, conversion or
+      // operand read is outstanding past B_end; 16-byte chunks XOR-swizzled by
+      // the head's low bits), then stored as whole lines, four heads per
+      // instruction, as in the bf16-cache kernel.  Only this wave touches its
+      // half, and the LDS operations of a wave execute in order.
+      static_assert(2 * 64 * 256 <= kCvBytes, "two waves' output staging fit one converted tile");
+      unsigned char* st = sh.cv[w4 >> 1] + (w4 & 1) * 16384;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
-      if (hbase + ht * 16 >= a.H) continue;              // a missing head tile
-      const int hp = hbase + ht * 16 + n16;
-      const float l_tot = sh.l[ht * 16 + n16];
-      const float m_fin = sh.m[ht * 16 + n16];
-      if (a.splits == 1) {
+      for (int ht = 0; ht < 4; ++ht) {
+        const int h = ht * 16 + n16;
+        const float l_tot = sh.l[h];
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* op = a.out + ((int64_t)r * a.H + hp) * kVDim + d_base + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           const v4f o = acc[ht][dt];
           uint2 pk;
-          pk.x = (uint32_t)f32_to_bf16_rne(o[0] * inv) | ((uint32_t)f32_to_bf16_rne(o[1] * inv) << 16);
-          pk.y = (uint32_t)f32_to_bf16_rne(o[2] * inv) | ((uint32_t)f32_to_bf16_rne(o[3] * inv) << 16);
-          *reinterpret_cast<uint2*>(op + dt * 16) = pk;
+          pk.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+          pk.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+          *reinterpret_cast<uint2*>(st + h * 256 + (((2 * dt + (g >> 1)) ^ n16) << 4) + 8 * (g & 1)) = pk;
         }
-        if (w4 == 0 && g == 0)
-          a.lse[(int64_t)r * a.H + hp] = l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : -INFINITY;
-      } else {
+        if (w4 == 0 && g == 0 && hbase + ht * 16 < a.H)
+          a.lse[(int64_t)r * a.H + hbase + h] = l_tot > 0.f ? (sh.m[h] + __log2f(l_tot)) * kLn2 : -INFINITY;
+      }
+      asm volatile("" ::: "memory");
+      const int c = lane & 15;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (hbase + 16 * (q >> 2) >= a.H) break;          // missing head tiles (the last ones)
+        const int h = 4 * q + (lane >> 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(st + h * 256 + ((c ^ (h & 15)) << 4));
+        *reinterpret_cast<uint4*>(a.out + ((int64_t)r * a.H + hbase + h) * kVDim + d_base + 8 * c) = v;
+      }
+    } else {
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        if (hbase + ht * 16 >= a.H) continue;            // a missing head tile
+        const int hp = hbase + ht * 16 + n16;
+        const float l_tot = sh.l[ht * 16 + n16];
+        const float m_fin = sh.m[ht * 16 + n16];
         const int64_t base = ((int64_t)sp * R + r) * a.H + hp;
         float* pa = a.part_acc + base * kVDim + d_base + 4 * g;
 #pragma unroll
