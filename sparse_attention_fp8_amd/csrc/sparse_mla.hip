@@ -453,6 +453,35 @@ __global__ void __launch_bounds__(64 * HT * TP) sparse_mla_kernel(MlaArgs a) {
       }
       if (dpart == 0 && g == 0)
         a.lse[(int64_t)r * a.H + hp] = l_tot > 0.f ? (m_pv[hh] + __log2f(l_tot)) * kLn2 : -INFINITY;
+    } else if constexpr (PVH == 1) {
+      // The wave's partial (16 heads x DW dims, fp32) is staged in tile
+      // buffer 0 (free: every wave is past two barriers since its last read,
+      // and no copy is outstanding), 16-byte chunks XOR-swizzled by the head,
+      // and stored as whole rows of DW dims: stored straight from the
+      // accumulators every instruction writes 64 bytes to each of 16 rows.
+      // Only this wave touches its part of the buffer, and the LDS operations
+      // of a wave execute in order.
+      constexpr int CH = DW / 4;                       // 16-byte chunks per head row
+      static_assert(NW * 16 * DW * 4 <= kTileBytes, "partial staging fits one tile buffer");
+      float* st = reinterpret_cast<float*>(sh.tile[0] + wave * (16 * DW * 4));
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const v4f o = acc[0][dt];
+        *reinterpret_cast<float4*>(st + n16 * DW + (((4 * dt + g) ^ n16) << 2)) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      asm volatile("" ::: "memory");
+      const int64_t base0 = ((int64_t)sp * R + r) * a.H + (hp0 - n16);
+#pragma unroll
+      for (int q = 0; q < 16 * CH / 64; ++q) {
+        const int hrow = (q * 64 + lane) / CH, c = (q * 64 + lane) % CH;
+        const float4 v = *reinterpret_cast<const float4*>(st + hrow * DW + ((c ^ hrow) << 2));
+        *reinterpret_cast<float4*>(a.part_acc + (base0 + hrow) * kVDim + d_base + 4 * c) = v;
+      }
+      if (dpart == 0 && g == 0) {
+        const int64_t base = base0 + n16;
+        a.part_ml[base * 2] = l_tot > 0.f ? m_pv[0] : kMaskSentinel;
+        a.part_ml[base * 2 + 1] = l_tot;
+      }
     } else {
       const int64_t base = ((int64_t)sp * R + r) * a.H + hp;
       float* pa = a.part_acc + base * kVDim + d_base + 4 * g;
