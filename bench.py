@@ -374,17 +374,22 @@ def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True
     torch.cuda.synchronize()
     ms_graph_each = start.elapsed_time(stop) / args.steps
 
+    # Each stage: `stage_rounds` replays of its graph (`reps` launches each),
+    # each replay bracketed by events; the median replay gives the average
+    # launch duration (one replay disturbed by a clock or power transient moves
+    # the median little, where it would move the mean by its full size).
     stage_ms = {}
-    stage_rounds = max(1, args.steps // reps)
+    stage_rounds = max(5, args.steps // reps)
     for stage in timed_stages:
         stage_graphs[stage].replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(stage_rounds):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(stage_rounds + 1)]
+        evs[0].record(stream)
+        for i in range(stage_rounds):
             stage_graphs[stage].replay()
-        e1.record(stream)
+            evs[i + 1].record(stream)
         torch.cuda.synchronize()
-        stage_ms[stage] = e0.elapsed_time(e1) / (stage_rounds * reps)
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(stage_rounds))
+        stage_ms[stage] = per[stage_rounds // 2] / reps
 
     alt_ms = stage_ms.pop(other_mla) if details else None
     total_bytes = nbytes["indexer"] + nbytes["topk"] + nbytes[mla_stage]
@@ -411,7 +416,8 @@ def measure(dsa, synth, name, args, kv="bf16", splits=0, seed=None, details=True
         "timing": f"HIP graph replays after {args.warmup} warm-up steps and {warm_replays * chain_len} more "
                   f"untimed steps ({WARM_S} s, clocks settled): a graph of {chain_len} steps (rotating {copies} "
                   f"cache copies) replayed {args.steps // chain_len} times plus {args.steps % chain_len} single-step "
-                  f"graphs; stage times from graphs of {reps} launches of one entry point",
+                  f"graphs; stage times: median of {stage_rounds} replays of a graph of {reps} launches of one "
+                  f"entry point",
         "rows": R,
     }
     if details:
